@@ -1,0 +1,157 @@
+// Internal declarations and device helpers of the gfx950 W4A16 library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace awq {
+
+// ---------------------------------------------------------------- layout constants
+// gfx950 packed layout, version 2: a 1 KiB unit holds 16 output rows x one group of 128
+// input channels. Lane l of a wavefront owns 16 bytes of a unit: row l % 16, channels
+// 32 (l / 16) + 0..31 of the group, as four 32-bit words of eight channels each.
+constexpr int kTileN = 16;        // output rows per unit
+constexpr int kGroup = 128;       // input channels per unit (the group size)
+constexpr int kUnitBytes = 1024;  // 16 rows x 128 channels x 4 bits
+constexpr int kLayoutVersion = 2;
+
+struct PackedLayout {
+  int64_t n_tiles;       // ceil(N / 16)
+  int64_t n_groups;      // K / 128
+  int64_t codes_off;     // byte offsets inside the packed buffer
+  int64_t scales_off;
+  int64_t zeros_off;     // -1 for the symmetric format
+  int64_t total_bytes;
+};
+
+inline PackedLayout make_layout(int64_t N, int64_t K, int32_t group, int32_t fmt) {
+  PackedLayout L;
+  L.n_tiles = (N + kTileN - 1) / kTileN;
+  L.n_groups = K / group;
+  L.codes_off = 0;
+  L.scales_off = L.n_tiles * L.n_groups * kUnitBytes;
+  int64_t end = L.scales_off + L.n_tiles * L.n_groups * kTileN * 2;
+  if (fmt == 0) {
+    L.zeros_off = (end + 255) / 256 * 256;
+    end = L.zeros_off + L.n_tiles * L.n_groups * (kTileN / 2);
+  } else {
+    L.zeros_off = -1;
+  }
+  L.total_bytes = (end + 255) / 256 * 256;
+  return L;
+}
+
+// ------------------------------------------------------------ launchers (per file)
+hipError_t launch_channel_scale(const uint16_t* x_cal, int64_t rows, int64_t K, double alpha,
+                                uint16_t* s_c, uint16_t* inv_s_c, hipStream_t st);
+hipError_t launch_pack(const uint16_t* w, const uint16_t* s_c, int64_t N, int64_t K,
+                       int32_t group, int32_t fmt, int32_t* qweight, uint16_t* scales,
+                       int32_t* qzeros, hipStream_t st);
+hipError_t launch_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
+                         int64_t N, int64_t K, int32_t group, int32_t fmt, void* packed,
+                         hipStream_t st);
+hipError_t launch_dequant_canonical(const int32_t* qweight, const uint16_t* scales,
+                                    const int32_t* qzeros, int64_t N, int64_t K, int32_t group,
+                                    int32_t fmt, uint16_t* w_out, hipStream_t st);
+hipError_t launch_dequant_packed(const void* packed, int64_t N, int64_t K, int32_t group,
+                                 int32_t fmt, uint16_t* w_out, hipStream_t st);
+
+size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemv(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
+                       int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y, void* ws,
+                       size_t ws_bytes, hipStream_t st);
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
+                       int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y, void* ws,
+                       size_t ws_bytes, hipStream_t st);
+
+// ------------------------------------------------------------------ device helpers
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+__host__ __device__ inline double f16_bits_to_f64(uint16_t h) {
+  const int e = (h >> 10) & 0x1F;
+  const int f = h & 0x3FF;
+  double mag;
+  if (e == 0x1F) {
+    mag = f ? __builtin_nan("") : __builtin_inf();
+  } else if (e == 0) {
+    mag = __builtin_ldexp(static_cast<double>(f), -24);
+  } else {
+    mag = __builtin_ldexp(static_cast<double>(f + 1024), e - 25);
+  }
+  return (h & 0x8000) ? -mag : mag;
+}
+
+// Nearest binary16 to a float64, ties to even, subnormals kept, overflow to infinity.
+// The value is scaled by a power of two (exact) so that one rint() in float64 does the
+// rounding: in the subnormal range the units are 2^-24, elsewhere 2^(e-10).
+__host__ __device__ inline uint16_t f64_to_f16_rn(double d) {
+  const uint16_t sign = __builtin_signbit(d) ? 0x8000 : 0;
+  const double a = __builtin_fabs(d);
+  if (a != a) return 0x7E00;
+  if (a >= 65520.0) return sign | 0x7C00;  // 65520 ties to the even neighbour: infinity
+  if (a < 6.103515625e-05) {               // below 2^-14: subnormal units of 2^-24
+    const double m = __builtin_rint(__builtin_ldexp(a, 24));
+    return sign | static_cast<uint16_t>(m);  // m == 1024 is the smallest normal
+  }
+  int e;
+  (void)__builtin_frexp(a, &e);  // a = f * 2^e, f in [0.5, 1)  ->  a in [2^(e-1), 2^e)
+  const int ex = e - 1;          // -14 .. 15
+  const double m = __builtin_rint(__builtin_ldexp(a, 10 - ex));  // 1024 .. 2048
+  const int bits = ((ex + 15) << 10) + (static_cast<int>(m) - 1024);
+  return sign | static_cast<uint16_t>(bits);
+}
+
+// Four pairs of binary16 from one packed word in the gfx950 nibble order: pair p holds
+// channels (2p, 2p + 1) of the word as binary16 (off + q), off = 1024 for p = 0, 2 and
+// 64 for p = 1, 3. OR-ing a nibble into the fraction of 1024 (0x6400, unit 1) or of 64
+// (0x5400, unit 1/16, nibble at bits 4..7) yields the integer exactly.
+struct Pairs4 {
+  uint32_t p[4];
+};
+
+__device__ __forceinline__ Pairs4 unpack_word(uint32_t w) {
+  Pairs4 r;
+  const uint32_t w8 = w >> 8;
+  r.p[0] = (w & 0x000F000Fu) | 0x64006400u;
+  r.p[1] = (w & 0x00F000F0u) | 0x54005400u;
+  r.p[2] = (w8 & 0x000F000Fu) | 0x64006400u;
+  r.p[3] = (w8 & 0x00F000F0u) | 0x54005400u;
+  return r;
+}
+
+// binary16 bit patterns of -(1024 + z) and -(64 + z), duplicated in both halves.
+__device__ __forceinline__ uint32_t neg_off1024(uint32_t z) {
+  const uint32_t h = 0xE400u | z;
+  return h | (h << 16);
+}
+__device__ __forceinline__ uint32_t neg_off64(uint32_t z) {
+  const uint32_t h = 0xD400u | (z << 4);
+  return h | (h << 16);
+}
+
+__device__ __forceinline__ half2_t as_h2(uint32_t u) {
+  return __builtin_bit_cast(half2_t, u);
+}
+__device__ __forceinline__ uint32_t as_u32(half2_t h) {
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// Exact dequantization of one word: eight binary16 values (q - z) * s in channel order.
+// (off + q) - (off + z) is an exact small integer; one binary16 multiply rounds once.
+__device__ __forceinline__ void dequant_word(uint32_t w, uint32_t nz1024, uint32_t nz64,
+                                             half2_t s2, half2_t out[4]) {
+  const Pairs4 pr = unpack_word(w);
+  out[0] = (as_h2(pr.p[0]) + as_h2(nz1024)) * s2;
+  out[1] = (as_h2(pr.p[1]) + as_h2(nz64)) * s2;
+  out[2] = (as_h2(pr.p[2]) + as_h2(nz1024)) * s2;
+  out[3] = (as_h2(pr.p[3]) + as_h2(nz64)) * s2;
+}
+
+// Offset of channel pair p of a word: 1024 for p even, 64 for p odd.
+__host__ __device__ constexpr float pair_offset(int p) { return (p & 1) ? 64.0f : 1024.0f; }
+
+}  // namespace awq

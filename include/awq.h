@@ -1,0 +1,200 @@
+/*
+ * awq.h - C ABI of the W4A16 weight-only quantized linear layer for MI355X (gfx950).
+ *
+ * The layer computes y = X' . deq(Wq)^T where
+ *   - W[N, K] (row n = output channel) is stored as 4-bit codes q with one binary16
+ *     scale s and one 4-bit zero point z per group of `group` consecutive input
+ *     channels, deq(q) = (q - z) * s  ("The Ultimate Guide to Quantized LLMs: GPTQ",
+ *     section "Understanding Quantized Model Compression": per-block scaling factors
+ *     and zero points);
+ *   - a per-input-channel scale s_c has been folded into W before quantization,
+ *     W' = W diag(s_c), and X' = X diag(s_c)^-1 is applied to the activations
+ *     ("Quantization Paradigms for Edge Inference", section 3 "The Math Behind
+ *     Activation-Aware Protection (AWQ)", first equation);
+ *   - decode (a handful of activation rows) is served by a matrix-vector kernel and
+ *     batched decode / prefill by a matrix-core kernel (edgesiliconlab ?p=2015,
+ *     section "GEMM vs. GEMV Kernels and Batch Size Dynamics").
+ *
+ * Conventions shared by every entry point
+ *   - Element types: binary16 values travel as uint16_t bit patterns; packed 4-bit
+ *     words as int32_t (two's-complement view of the uint32 word).
+ *   - Canonical layouts (row-major, all contiguous):
+ *       qweight [N][K/8]   int32, element k of row n in bits 4*(k%8).. of word k/8
+ *       scales  [K/G][N]   binary16
+ *       qzeros  [K/G][N/8] int32, zero of column n in bits 4*(n%8).. of word n/8
+ *                          (asymmetric format only; NULL for the symmetric format)
+ *       X [M][K], y [M][N] binary16
+ *   - Formats: AWQ_FMT_ASYM (scale + zero point), AWQ_FMT_SYM8 (zero fixed at 8).
+ *   - Shapes: N % 8 == 0, K % group == 0, group == 128 (the only group size the
+ *     kernels are built for; others return AWQ_ERR_UNSUPPORTED), N*K < 2^32.
+ *   - Pointers marked "device" must be device (HBM) addresses on the current HIP
+ *     device, 16-byte aligned (AWQ_ERR_MISALIGNED otherwise). The library never
+ *     allocates, frees or retains a pointer: the caller owns every buffer.
+ *   - Every device entry point is asynchronous and ordered on `stream` (0 = the
+ *     null stream). All argument checks run before any launch; a rejected call
+ *     launches nothing. A launch failure returns AWQ_ERR_HIP; faults inside a
+ *     kernel surface at the caller's next synchronisation, as for any HIP kernel.
+ *   - The library holds no mutable global state; calls on different streams that
+ *     share no output or workspace buffer may run concurrently.
+ */
+#ifndef AWQ_H_
+#define AWQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define AWQ_OK 0
+#define AWQ_ERR_INVALID_ARG 1 /* NULL where a buffer is required, negative or
+                                 non-divisible size, unknown enum value        */
+#define AWQ_ERR_UNSUPPORTED 2 /* valid request the kernels are not built for   */
+#define AWQ_ERR_MISALIGNED 3  /* a device pointer is not 16-byte aligned       */
+#define AWQ_ERR_WORKSPACE 4   /* packed or workspace buffer smaller than needed */
+#define AWQ_ERR_HIP 5         /* the HIP runtime rejected a launch             */
+
+#define AWQ_FMT_ASYM 0
+#define AWQ_FMT_SYM8 1
+
+#define AWQ_LAYOUT_CANONICAL 0
+#define AWQ_LAYOUT_GFX950 1
+
+/* Static text for a status code (never NULL). */
+const char* awq_status_string(int status);
+
+/* Version of the gfx950 packed layout produced by awq_repack. */
+int awq_layout_version(void);
+
+/*
+ * awq_channel_scale - per-input-channel scale from calibration activations.
+ * "Quantization Paradigms for Edge Inference", section 3: salient channels are found
+ * from activation magnitudes over a calibration set; the scale is a power of that
+ * magnitude.
+ *   m_k        = (sum over r < rows of |x_cal[r][k]|) / rows     (float64)
+ *   s_c[k]     = binary16(m_k ^ alpha), or 1.0 where m_k == 0
+ *   inv_s_c[k] = binary16(1 / s_c[k])
+ * x_cal   device, [rows][K] binary16, read only. 1 <= rows <= 8192.
+ * s_c     device, [K] binary16, written.
+ * inv_s_c device, [K] binary16, written; may be NULL.
+ * alpha   exponent in [0, 1]. alpha == 0.5 gives the correctly rounded square root;
+ *         other values go through the device pow().
+ * Errors: INVALID_ARG (NULL x_cal/s_c, rows or K out of range, alpha outside [0,1]
+ *         or NaN), MISALIGNED, HIP.
+ */
+int awq_channel_scale(const uint16_t* x_cal, int64_t rows, int64_t K, double alpha,
+                      uint16_t* s_c, uint16_t* inv_s_c, hipStream_t stream);
+
+/*
+ * awq_pack - fold the channel scale into W, quantize each group to 4 bits by
+ * round-to-nearest and pack (edgesiliconlab ?p=2015, section "What Is the Core
+ * Difference Between AWQ and GPTQ Quantization?": the scaled matrix is quantized
+ * with plain round-to-nearest; section "Kernel Execution: Marlin vs. ExLlamaV2 INT4
+ * GEMM Micro-Architecture", item 3: 4-bit values packed side by side in a word).
+ * For each output row n and group g (v = the group's folded weights
+ * binary16(W[n][k] * s_c[k]); rint = round half to even):
+ *   AWQ_FMT_ASYM: lo = min(min v, 0), hi = max(max v, 0)
+ *                 s = max(binary16((hi - lo) / 15), 2^-24)
+ *                 z = clamp(rint(-lo / s), 0, 15)
+ *   AWQ_FMT_SYM8: s = max(binary16(max|v| / 7), 2^-24), z = 8
+ *   q = clamp(rint(v / s) + z, 0, 15)
+ * w       device, [N][K] binary16, read only.
+ * s_c     device, [K] binary16 channel scale; NULL means s_c = 1 (plain RTN).
+ * qweight device, [N][K/8] int32, written (canonical layout above).
+ * scales  device, [K/group][N] binary16, written.
+ * qzeros  device, [K/group][N/8] int32, written for ASYM; must be NULL for SYM8.
+ * Inputs must be finite and the fold must not overflow binary16.
+ * Errors: INVALID_ARG, UNSUPPORTED (group), MISALIGNED, HIP.
+ */
+int awq_pack(const uint16_t* w, const uint16_t* s_c, int64_t N, int64_t K, int32_t group,
+             int32_t fmt, int32_t* qweight, uint16_t* scales, int32_t* qzeros,
+             hipStream_t stream);
+
+/* Bytes of the gfx950 packed buffer for an N x K layer (0 if the shape is invalid). */
+size_t awq_repacked_bytes(int64_t N, int64_t K, int32_t group, int32_t fmt);
+
+/*
+ * awq_repack - canonical (qweight, scales, qzeros) to the gfx950 packed layout read
+ * by awq_gemv, awq_gemm and awq_dequant(AWQ_LAYOUT_GFX950). A pure integer
+ * permutation: no value changes. The layout (version awq_layout_version() == 2):
+ *   rows padded to Np = 16 * ceil(N / 16) (padding rows: codes 0, scale 0, zero 0);
+ *   codes  at offset 0: unit (t, g) for t < Np/16, g < K/128 at ((t * K/128) + g) * 1024;
+ *          in a unit, lane l (0..63) owns bytes [16 l, 16 l + 16): row n = 16 t + l % 16,
+ *          four words, word i holding channel k = 128 g + 32 (l / 16) + 8 i + e, e < 8,
+ *          at nibble position (e >> 1) + 4 * (e & 1);
+ *   scales at offset Np * K / 2: binary16 [(t * K/128 + g) * 16 + l % 16];
+ *   zeros  (ASYM) at the next 256-byte boundary: 4-bit [(t * K/128 + g) * 16 + r],
+ *          nibble (r % 8) of 32-bit word ((t * K/128 + g) * 2 + r / 8).
+ * One 128-bit load per lane of a wavefront reads a whole unit; a lane's word i is the
+ * B operand of step i of v_mfma_f32_16x16x32_f16 for its row.
+ * qweight, scales: device, read only. qzeros: device for ASYM, NULL for SYM8.
+ * packed: device, at least awq_repacked_bytes() bytes, written.
+ * Errors: INVALID_ARG, UNSUPPORTED, MISALIGNED, WORKSPACE (packed_bytes too small), HIP.
+ */
+int awq_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
+               int64_t N, int64_t K, int32_t group, int32_t fmt, void* packed,
+               size_t packed_bytes, hipStream_t stream);
+
+/*
+ * awq_dequant - W_d[n][k] = binary16((q - z) * s), one rounding, bit-exact.
+ * layout AWQ_LAYOUT_CANONICAL: w = qweight, with scales and qzeros (NULL for SYM8).
+ * layout AWQ_LAYOUT_GFX950:    w = packed buffer; scales and qzeros must be NULL.
+ * w_out  device, [N][K] binary16, written.
+ * Errors: INVALID_ARG, UNSUPPORTED, MISALIGNED, HIP.
+ */
+int awq_dequant(const void* w, const uint16_t* scales, const int32_t* qzeros,
+                int32_t layout, int64_t N, int64_t K, int32_t group, int32_t fmt,
+                uint16_t* w_out, hipStream_t stream);
+
+/*
+ * Workspace bytes that awq_gemv / awq_gemm need for an M x N x K call. The kernels of
+ * this version keep every partial sum inside a workgroup and need none (0 is
+ * returned); the argument is part of the ABI so that a caller that provides a buffer
+ * keeps working with versions that split K across workgroups.
+ */
+size_t awq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group);
+
+/*
+ * awq_gemv - decode product for 1 <= M <= 8 activation rows (edgesiliconlab ?p=2015,
+ * sections "The Mathematics of Memory Bandwidth Saturation" and "GEMM vs. GEMV
+ * Kernels and Batch Size Dynamics": at batch 1 the product streams every weight once
+ * and is bound by memory bandwidth).
+ *   y[m][n] = binary16( sum_k X'[m][k] * (q[n][k] - z[g][n]) * s[g][n] ),
+ *   X'[m][k] = binary16(x[m][k] * inv_s_c[k]) (or x itself when inv_s_c is NULL),
+ * accumulated in float32. Result within 2e-3 of the exact product of the
+ * dequantized weights, relative to max|y|.
+ * x       device, [M][K] binary16.   inv_s_c device, [K] binary16, or NULL.
+ * packed  device, gfx950 layout from awq_repack for (N, K, group, fmt).
+ * y       device, [M][N] binary16, written.
+ * ws      device workspace of ws_bytes >= awq_workspace_bytes() bytes, or NULL with
+ *         ws_bytes == 0.
+ * M == 0 returns AWQ_OK without launching. Deterministic: the same inputs give the
+ * same bits on every call.
+ * Errors: INVALID_ARG, UNSUPPORTED (M > 8, group), MISALIGNED, WORKSPACE, HIP.
+ */
+int awq_gemv(const uint16_t* x, const uint16_t* inv_s_c, const void* packed, int64_t M,
+             int64_t N, int64_t K, int32_t group, int32_t fmt, uint16_t* y, void* ws,
+             size_t ws_bytes, hipStream_t stream);
+
+/*
+ * awq_gemm - batched-decode / prefill product for any M >= 1 on the matrix cores
+ * (edgesiliconlab ?p=2015, "GEMM vs. GEMV Kernels and Batch Size Dynamics": larger
+ * batches turn the product into a matrix-matrix multiply; section "Kernel Execution:
+ * Marlin vs. ExLlamaV2 INT4 GEMM Micro-Architecture": weights are unpacked to
+ * binary16 just before the matrix instruction). Same arguments, math and accuracy as
+ * awq_gemv; the dequantized weights fed to the matrix cores are exactly W_d.
+ * Errors: INVALID_ARG, UNSUPPORTED, MISALIGNED, WORKSPACE, HIP.
+ */
+int awq_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* packed, int64_t M,
+             int64_t N, int64_t K, int32_t group, int32_t fmt, uint16_t* y, void* ws,
+             size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AWQ_H_ */

@@ -1,0 +1,133 @@
+"""The C-ABI library without a GPU: it loads, exports every declared entry point, and
+rejects bad arguments with the documented status before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "awq.h")
+
+awq = pytest.importorskip("bit_weight_only_w4a16_amd.awq")
+
+OK, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE, HIP = 0, 1, 2, 3, 4, 5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(awq_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(awq.LIB_PATH):
+        pytest.skip("library not built")
+    return awq.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(awq.EXPORTS) == names
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        s = awq.status_string(code)
+        assert isinstance(s, str) and s
+    assert awq.status_string(99) == "unknown status"
+    assert awq.awq_layout_version() == 2
+
+
+def test_sizes():
+    # codes N*K/2 + scales 2*N*K/128 + zeros N*K/256, regions 256-byte aligned
+    assert awq.awq_repacked_bytes(4096, 4096) == 8388608 + 262144 + 65536
+    assert awq.awq_repacked_bytes(4096, 4096, 128, awq.FMT_SYM8) == 8388608 + 262144
+    assert awq.awq_repacked_bytes(100, 256) == 0          # N % 8 != 0
+    assert awq.awq_repacked_bytes(64, 200) == 0           # K % 128 != 0
+    assert awq.awq_repacked_bytes(64, 256, 64) == 0       # unsupported group
+    assert awq.awq_workspace_bytes(0, 4096, 4096) == 0
+    assert awq.awq_workspace_bytes(1, 4096, 4096) == 0     # no split-K in this version
+
+
+def test_padded_layout_size():
+    # 72 rows -> 5 tiles of 16; K = 256 -> 2 groups of 128
+    codes = 5 * 2 * 1024
+    scales = 5 * 2 * 16 * 2
+    zeros_off = (codes + scales + 255) // 256 * 256
+    total = (zeros_off + 5 * 2 * 8 + 255) // 256 * 256
+    assert awq.awq_repacked_bytes(72, 256) == total
+    assert awq.awq_repacked_bytes(72, 256, 128, awq.FMT_SYM8) == (codes + scales + 255) // 256 * 256
+
+
+P = 4096  # an aligned stand-in address; never dereferenced because validation fails
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, None, P, 1, 64, 128, 128, 0, P, None, 0, None), INVALID),      # x NULL
+    ((P, None, None, 1, 64, 128, 128, 0, P, None, 0, None), INVALID),      # packed NULL
+    ((P, None, P, 1, 64, 128, 128, 0, None, None, 0, None), INVALID),      # y NULL
+    ((P, None, P, 1, 60, 128, 128, 0, P, None, 0, None), INVALID),         # N % 8
+    ((P, None, P, 1, 64, 100, 128, 0, P, None, 0, None), INVALID),         # K % group
+    ((P, None, P, 1, 64, 128, 128, 2, P, None, 0, None), INVALID),         # fmt
+    ((P, None, P, -1, 64, 128, 128, 0, P, None, 0, None), INVALID),        # M < 0
+    ((P, None, P, 1, 64, 256, 64, 0, P, None, 0, None), UNSUPPORTED),      # group 64
+    ((P + 2, None, P, 1, 64, 128, 128, 0, P, None, 0, None), MISALIGNED),  # x
+    ((P, P + 8, P, 1, 64, 128, 128, 0, P, None, 0, None), MISALIGNED),     # inv_s_c
+    ((P, None, P, 1, 64, 128, 128, 0, P, None, 16, None), INVALID),        # ws NULL, bytes
+    ((P, None, P, 9, 64, 128, 128, 0, P, None, 0, None), UNSUPPORTED),     # M > 8 (gemv)
+    ((None, None, None, 0, 64, 128, 128, 0, None, None, 0, None), OK),     # M == 0: no-op
+])
+def test_gemv_validation(lib, args, code):
+    assert lib.awq_gemv(*args) == code
+
+
+def test_gemm_validation(lib):
+    assert lib.awq_gemm(None, None, None, 0, 64, 128, 128, 0, None, None, 0, None) == OK
+    assert lib.awq_gemm(P, None, P, 9, 64, 100, 128, 0, P, None, 0, None) == INVALID
+    assert lib.awq_gemm(P, None, P, 9, 64, 256, 32, 0, P, None, 0, None) == UNSUPPORTED
+    assert lib.awq_gemm(P, None, P + 4, 9, 64, 128, 128, 0, P, None, 0, None) == MISALIGNED
+
+
+def test_pack_and_repack_validation(lib):
+    # qzeros must be given for the asymmetric format and NULL for the symmetric one
+    assert lib.awq_pack(P, None, 64, 128, 128, 0, P, P, None, None) == INVALID
+    assert lib.awq_pack(P, None, 64, 128, 128, 1, P, P, P, None) == INVALID
+    assert lib.awq_pack(None, None, 64, 128, 128, 0, P, P, P, None) == INVALID
+    assert lib.awq_pack(P, P + 2, 64, 128, 128, 0, P, P, P, None) == MISALIGNED
+    assert lib.awq_repack(P, P, P, 64, 128, 128, 0, P, 16, None) == WORKSPACE
+    assert lib.awq_repack(P, P, None, 64, 128, 128, 0, P, 1 << 20, None) == INVALID
+    assert lib.awq_dequant(P, P, P, 1, 64, 128, 128, 0, P, None) == INVALID   # gfx950 + scales
+    assert lib.awq_dequant(P, None, None, 7, 64, 128, 128, 1, P, None) == INVALID
+    assert lib.awq_dequant(P, None, None, 0, 64, 128, 128, 1, P, None) == INVALID  # no scales
+
+
+def test_channel_scale_validation(lib):
+    assert lib.awq_channel_scale(None, 32, 512, 0.5, P, None, None) == INVALID
+    assert lib.awq_channel_scale(P, 0, 512, 0.5, P, None, None) == INVALID
+    assert lib.awq_channel_scale(P, 9000, 512, 0.5, P, None, None) == INVALID
+    assert lib.awq_channel_scale(P, 32, 512, 1.5, P, None, None) == INVALID
+    assert lib.awq_channel_scale(P, 32, 512, float("nan"), P, None, None) == INVALID
+    assert lib.awq_channel_scale(P, 32, 512, 0.5, P + 2, None, None) == MISALIGNED
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        awq.awq_gemv(torch.zeros(1, 128, dtype=torch.float16), None,
+                     torch.zeros(16, dtype=torch.uint8), 64, 128)
+
+
+def test_ctypes_signature_matches_header():
+    text = open(HEADER).read()
+    for name, (_res, argtypes) in awq._SIGNATURES.items():
+        m = re.search(r"\b" + name + r"\s*\(([^)]*)\)\s*;", text, flags=re.S)
+        assert m, name
+        params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
+        assert len(params) == len(argtypes), name
+    _ = ctypes

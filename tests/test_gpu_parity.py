@@ -1,0 +1,317 @@
+"""GPU path (through the C ABI) against the CPU oracle, element by element.
+
+Bit-exact: channel scales, packed codes / scales / zeros, dequantized weights (both
+layouts). Within max|y - y_ref| / max|y_ref| <= 2e-3: the GEMV and GEMM outputs
+against the float64 product of the oracle's dequantized weights.
+Small shapes cover several tiles and ragged tails; the full layer shapes of the
+benchmark are checked on sampled output rows the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from bit_weight_only_w4a16_amd import synth
+
+torch = pytest.importorskip("torch")
+awq = pytest.importorskip("bit_weight_only_w4a16_amd.awq")
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+DEV = "cuda"
+
+
+def f16bits(a):
+    return np.asarray(a, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def bits(t):
+    return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def rel_err(y, y_ref):
+    y = np.asarray(y, dtype=np.float64)
+    return np.max(np.abs(y - y_ref)) / max(np.max(np.abs(y_ref)), 1e-30)
+
+
+def gpu_quantize(w, x_cal, fmt, use_scale=True):
+    w_d = to_dev(w)
+    s_c = inv = None
+    if use_scale:
+        s_c, inv = awq.awq_channel_scale(to_dev(x_cal), 0.5)
+    qweight, scales, qzeros = awq.awq_pack(w_d, s_c, 128, fmt)
+    n, k = w.shape
+    packed = awq.awq_repack(qweight, scales, qzeros, n, k, 128, fmt)
+    return {"s_c": s_c, "inv": inv, "qweight": qweight, "scales": scales, "qzeros": qzeros,
+            "packed": packed}
+
+
+def oracle_quantize(w, x_cal, fmt, use_scale=True, rows=None):
+    s = inv = None
+    if use_scale:
+        s, inv = oracle.channel_scale(x_cal, 0.5)
+    ww = w if rows is None else w[rows]
+    layer = oracle.quantize_layer(ww, s, 128, fmt)
+    layer["s_c"], layer["inv"] = s, inv
+    return layer
+
+
+def check_bits_exact(g, o, fmt, rows=None, n=None):
+    qw = g["qweight"].cpu().numpy()
+    sc = bits(g["scales"])
+    if rows is not None:
+        qw = qw[rows]
+        sc = sc[:, rows]
+    assert np.array_equal(qw, o["qweight"])
+    assert np.array_equal(sc, o["scales_bits"])
+    if fmt == awq.FMT_ASYM:
+        zg = oracle.unpack_zeros(g["qzeros"].cpu().numpy())
+        if rows is not None:
+            zg = zg[:, rows]
+        assert np.array_equal(zg, o["zeros"])
+    else:
+        assert g["qzeros"] is None
+
+
+# ----------------------------------------------------------------- channel scale
+
+@pytest.mark.parametrize("k", [512, 4096, 11008])
+@pytest.mark.parametrize("alpha", [0.5, 0.0, 1.0, 0.25])
+def test_channel_scale_bit_exact(k, alpha):
+    d = synth.layer_inputs(1, 1, 8, k)
+    x_cal = d["x_cal"].copy()
+    x_cal[:, 3] = 0                        # a dead channel: scale 1
+    s, inv = awq.awq_channel_scale(to_dev(x_cal), alpha)
+    s_ref, inv_ref = oracle.channel_scale(x_cal, alpha)
+    assert np.array_equal(bits(s), f16bits(s_ref))
+    assert np.array_equal(bits(inv), f16bits(inv_ref))
+
+
+def test_channel_scale_midpoint_squares():
+    """Means that are exactly squares of binary16 midpoints (square root ties)."""
+    k, rows = 256, 32
+    rng = np.random.default_rng(0)
+    e = rng.integers(-1, 3, size=k)
+    odd = rng.integers(1024, 2048, size=k) * 2 + 1      # 12-bit odd significand
+    mid = np.ldexp(odd.astype(np.float64), e - 11)     # binary16 midpoints in [0.5, 8)
+    total = rows * mid * mid                            # column sum for mean = mid^2
+    x = np.zeros((rows, k), dtype=np.float16)
+    ok = np.zeros(k, dtype=bool)
+    for j in range(k):
+        rest, parts = total[j], []
+        for _ in range(4):                              # greedy split, rounding down
+            v = np.float16(rest)
+            if float(v) > rest:
+                v = np.nextafter(v, np.float16(0))
+            parts.append(v)
+            rest -= float(v)
+        ok[j] = rest == 0
+        x[:4, j] = parts
+    assert ok.sum() > 200
+    x[:, ~ok] = 1
+    s, _ = awq.awq_channel_scale(to_dev(x), 0.5)
+    s_ref, _ = oracle.channel_scale(x, 0.5)
+    m = np.abs(x.astype(np.float64)).sum(axis=0) / rows
+    assert np.array_equal(m[ok], (mid * mid)[ok])       # the means really are squares
+    assert np.array_equal(bits(s), f16bits(s_ref))
+
+
+# -------------------------------------------------------------------- pack, repack
+
+SMALL = [(512, 512), (200, 1024), (1000, 384), (64, 128), (72, 256), (4096, 4096)]
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("n,k", SMALL)
+def test_pack_bit_exact(n, k, fmt):
+    d = synth.layer_inputs(0, 1, n, k)
+    g = gpu_quantize(d["w"], d["x_cal"], fmt)
+    o = oracle_quantize(d["w"], d["x_cal"], fmt)
+    assert np.array_equal(bits(g["s_c"]), f16bits(o["s_c"]))
+    check_bits_exact(g, o, fmt)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_pack_without_channel_scale(fmt):
+    d = synth.layer_inputs(0, 1, 256, 512)
+    g = gpu_quantize(d["w"], d["x_cal"], fmt, use_scale=False)
+    o = oracle_quantize(d["w"], d["x_cal"], fmt, use_scale=False)
+    check_bits_exact(g, o, fmt)
+
+
+def adversarial_weights(n=64, k=512, seed=3):
+    """Groups built to hit the rounding edges: exact ties in v/s, all-zero, constant,
+    single-sign, subnormal-range and wide-range groups."""
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float16).astype(np.float64)
+    gs = k // 128
+    for r in range(n):
+        gi = r % gs
+        sl = slice(gi * 128, gi * 128 + 128)
+        kind = r % 8
+        if kind == 0:
+            w[r, sl] = 0.0
+        elif kind == 1:
+            w[r, sl] = 0.375
+        elif kind == 2:
+            w[r, sl] = -np.abs(w[r, sl])
+        elif kind == 3:                      # on-grid with half-step ties
+            s = 2.0 ** -6
+            q = rng.integers(0, 31, size=128) / 2.0
+            q[0], q[1] = 0, 15
+            w[r, sl] = (q - 7) * s
+        elif kind == 4:                      # tiny values (binary16 subnormals)
+            w[r, sl] = rng.integers(-40, 41, size=128) * 2.0 ** -24
+        elif kind == 5:                      # wide range
+            w[r, sl] = rng.standard_normal(128) * 1000
+        elif kind == 6:                      # one large outlier
+            w[r, sl.start + 5] = 60000.0 if r % 16 < 8 else -60000.0
+    return w.astype(np.float16)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_pack_adversarial_groups(fmt):
+    w = adversarial_weights()
+    x_cal = np.ones((32, w.shape[1]), dtype=np.float16)
+    g = gpu_quantize(w, x_cal, fmt)
+    o = oracle_quantize(w, x_cal, fmt)
+    check_bits_exact(g, o, fmt)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("n,k", [(512, 512), (200, 1024), (72, 256), (4096, 4096)])
+def test_dequant_bit_exact_both_layouts(n, k, fmt):
+    d = synth.layer_inputs(0, 1, n, k)
+    g = gpu_quantize(d["w"], d["x_cal"], fmt)
+    o = oracle_quantize(d["w"], d["x_cal"], fmt)
+    ref = f16bits(o["w_d"])
+    w1 = awq.awq_dequant(g["packed"], None, None, awq.LAYOUT_GFX950, n, k, 128, fmt)
+    assert np.array_equal(bits(w1), ref)
+    w0 = awq.awq_dequant(g["qweight"], g["scales"], g["qzeros"], awq.LAYOUT_CANONICAL,
+                         n, k, 128, fmt)
+    assert np.array_equal(bits(w0), ref)
+
+
+def test_dequant_adversarial():
+    w = adversarial_weights(n=128, k=1024, seed=9)
+    x_cal = np.ones((32, w.shape[1]), dtype=np.float16)
+    for fmt in (0, 1):
+        g = gpu_quantize(w, x_cal, fmt)
+        o = oracle_quantize(w, x_cal, fmt)
+        wd = awq.awq_dequant(g["packed"], None, None, awq.LAYOUT_GFX950, 128, 1024, 128, fmt)
+        assert np.array_equal(bits(wd), f16bits(o["w_d"]))
+
+
+# ----------------------------------------------------------------- products (small)
+
+def product_case(n, k, m, fmt, seed=0):
+    d = synth.layer_inputs(seed, m, n, k)
+    g = gpu_quantize(d["w"], d["x_cal"], fmt)
+    o = oracle_quantize(d["w"], d["x_cal"], fmt)
+    y_ref = oracle.matmul_ref(d["x"], o["w_d"], o["inv"])
+    return d, g, o, y_ref
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("n,k", [(512, 512), (200, 1024), (72, 256), (1000, 3072)])
+def test_gemv_parity(n, k, m, fmt):
+    d, g, o, y_ref = product_case(n, k, m, fmt)
+    x = to_dev(d["x"])
+    ws = awq.workspace(m, n, k, DEV)
+    y = awq.awq_gemv(x, g["inv"], g["packed"], n, k, 128, fmt, ws=ws)
+    assert rel_err(y.cpu().numpy(), y_ref) <= TOL
+    y2 = awq.awq_gemv(x, g["inv"], g["packed"], n, k, 128, fmt, ws=None)   # no split-K
+    assert rel_err(y2.cpu().numpy(), y_ref) <= TOL
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("m", [1, 7, 16, 33, 64, 130])
+@pytest.mark.parametrize("n,k", [(512, 512), (200, 1024), (72, 256)])
+def test_gemm_parity(n, k, m, fmt):
+    d, g, o, y_ref = product_case(n, k, m, fmt)
+    y = awq.awq_gemm(to_dev(d["x"]), g["inv"], g["packed"], n, k, 128, fmt)
+    assert rel_err(y.cpu().numpy(), y_ref) <= TOL
+
+
+def test_products_with_prescaled_activations():
+    """inv_s_c NULL: the caller passes X' = X * inv_s_c already in binary16."""
+    n, k, m = 256, 1024, 3
+    d, g, o, _ = product_case(n, k, m, 0)
+    xs = oracle.fp16_rn(oracle.as_f64(d["x"]) * o["inv"][None, :]).astype(np.float16)
+    y_ref = oracle.matmul_ref(xs, o["w_d"])
+    for fn in (awq.awq_gemv, awq.awq_gemm):
+        y = fn(to_dev(xs), None, g["packed"], n, k, 128, 0, ws=awq.workspace(m, n, k, DEV))
+        assert rel_err(y.cpu().numpy(), y_ref) <= TOL
+
+
+def test_zero_weights_give_zero_output():
+    n, k = 128, 512
+    w = np.zeros((n, k), dtype=np.float16)
+    x = synth.activations(2, k, 5, np.arange(5))
+    g = gpu_quantize(w, np.ones((32, k), np.float16), 0)
+    for fn in (awq.awq_gemv, awq.awq_gemm):
+        y = fn(to_dev(x), g["inv"], g["packed"], n, k, 128, 0, ws=awq.workspace(2, n, k, DEV))
+        assert torch.count_nonzero(y).item() == 0
+
+
+def test_m_zero_is_a_no_op():
+    n, k = 64, 128
+    g = gpu_quantize(synth.weights(n, k, 1), np.ones((32, k), np.float16), 0)
+    y = torch.full((0, n), 7.0, dtype=torch.float16, device=DEV)
+    x = torch.zeros((0, k), dtype=torch.float16, device=DEV)
+    awq.awq_gemv(x, None, g["packed"], n, k, y=y)
+    awq.awq_gemm(x, None, g["packed"], n, k, y=y)
+
+
+@pytest.mark.parametrize("fn", ["gemv", "gemm"])
+def test_products_deterministic(fn):
+    n, k, m = 4096, 4096, 1 if fn == "gemv" else 96
+    d, g, o, y_ref = product_case(n, k, m, 0)
+    x = to_dev(d["x"])
+    f = awq.awq_gemv if fn == "gemv" else awq.awq_gemm
+    ys = [f(x, g["inv"], g["packed"], n, k) for _ in range(5)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
+    assert rel_err(ys[0].cpu().numpy(), y_ref) <= TOL
+
+
+# ----------------------------------------------- full layer shapes, sampled outputs
+
+FULL = [
+    # (name, n, k, m, fmt, fn)
+    ("7b_qkvo_m1", 4096, 4096, 1, 0, "gemv"),
+    ("7b_gateup_m1", 11008, 4096, 1, 0, "gemv"),
+    ("7b_down_m1", 4096, 11008, 1, 0, "gemv"),
+    ("batched_m8", 11008, 4096, 8, 0, "gemv"),
+    ("batched_m16", 11008, 4096, 16, 0, "gemm"),
+    ("batched_m64", 11008, 4096, 64, 0, "gemm"),
+    ("prefill_qkv_m2048", 6144, 4096, 2048, 0, "gemm"),
+    ("prefill_down_m2048", 4096, 14336, 2048, 0, "gemm"),
+    ("70b_up_sym_m1", 28672, 8192, 1, 1, "gemv"),
+    ("70b_down_asym_m1", 8192, 28672, 1, 0, "gemv"),
+    ("70b_up_asym_m256", 28672, 8192, 256, 0, "gemm"),
+]
+
+
+@pytest.mark.parametrize("name,n,k,m,fmt,fn", FULL, ids=[c[0] for c in FULL])
+def test_full_shape_sampled(name, n, k, m, fmt, fn):
+    d = synth.layer_inputs(1, m, n, k)
+    g = gpu_quantize(d["w"], d["x_cal"], fmt)
+    rng = np.random.default_rng(42)
+    blocks = np.unique(np.concatenate([rng.choice(n // 8, 6, replace=False), [0, n // 8 - 1]]))
+    rows = (blocks[:, None] * 8 + np.arange(8)[None, :]).ravel()
+    o = oracle_quantize(d["w"], d["x_cal"], fmt, rows=rows)
+    check_bits_exact(g, o, fmt, rows=rows)
+    x = to_dev(d["x"])
+    ws = awq.workspace(m, n, k, DEV)
+    f = awq.awq_gemv if fn == "gemv" else awq.awq_gemm
+    y = f(x, g["inv"], g["packed"], n, k, 128, fmt, ws=ws).cpu().numpy()
+    y_ref = oracle.matmul_ref(d["x"], o["w_d"], o["inv"])      # [m, len(rows)]
+    assert rel_err(y[:, rows], y_ref) <= TOL
+    assert np.all(np.isfinite(y))
