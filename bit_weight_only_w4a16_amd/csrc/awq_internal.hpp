@@ -66,6 +66,25 @@ hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* p
                        size_t ws_bytes, hipStream_t st);
 
 // ------------------------------------------------------------------ device helpers
+// Buffer resource over [base, base + bytes): loads take a wavefront-uniform SGPR offset
+// plus a per-lane VGPR offset, so streaming through the weights costs no 64-bit address
+// arithmetic; an offset past `bytes` reads 0. Word 3 is the gfx9 raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+  const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(voff), static_cast<int>(soff), 0);
+}
+__device__ __forceinline__ uint32_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(voff), static_cast<int>(soff), 0);
+}
+
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
@@ -113,13 +132,23 @@ struct Pairs4 {
   uint32_t p[4];
 };
 
+// (a & mask) | magic in one v_and_or_b32. gfx9 VOP3 encodings take no literal
+// constants, so left to itself the compiler splits this into a v_and and a v_or with
+// literals; here the mask sits in an SGPR and the magic in a VGPR (one SGPR operand:
+// the constant-bus limit).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
+  return r;
+}
+
 __device__ __forceinline__ Pairs4 unpack_word(uint32_t w) {
   Pairs4 r;
   const uint32_t w8 = w >> 8;
-  r.p[0] = (w & 0x000F000Fu) | 0x64006400u;
-  r.p[1] = (w & 0x00F000F0u) | 0x54005400u;
-  r.p[2] = (w8 & 0x000F000Fu) | 0x64006400u;
-  r.p[3] = (w8 & 0x00F000F0u) | 0x54005400u;
+  r.p[0] = and_or(w, 0x000F000Fu, 0x64006400u);
+  r.p[1] = and_or(w, 0x00F000F0u, 0x54005400u);
+  r.p[2] = and_or(w8, 0x000F000Fu, 0x64006400u);
+  r.p[3] = and_or(w8, 0x00F000F0u, 0x54005400u);
   return r;
 }
 

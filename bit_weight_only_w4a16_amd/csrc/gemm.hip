@@ -60,7 +60,8 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
   constexpr int A_VEC = BM * (kGroup / 8) / kGThreads;  // 16-byte X' vectors per thread
   __shared__ __attribute__((aligned(16))) _Float16 xs[BM * kLdsStride];
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
+  const int lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 15, p = lane >> 4;
 
@@ -72,19 +73,18 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
   const int ng = a.n_groups;
 
   // this wavefront's weight tiles (clamped: tiles past the last one are read but their
-  // rows are >= N and never stored)
-  const uint4* bptr[WN];
-  const uint16_t* sptr[WN];
-  const uint32_t* zptr[WN];
+  // rows are >= N and never stored), as buffer resources: the per-group offset is
+  // uniform (SGPR), the per-lane offset constant
+  __amdgpu_buffer_rsrc_t rb[WN], rs[WN], rz[WN];
+  const bool asym = a.zeros_off >= 0;
 #pragma unroll
   for (int j = 0; j < WN; ++j) {
     const int64_t tile = min(n_blk / kTileN + wn * WN + j, a.n_tiles - 1);
-    bptr[j] = reinterpret_cast<const uint4*>(a.packed) + tile * ng * 64 + lane;
-    sptr[j] = reinterpret_cast<const uint16_t*>(a.packed + a.scales_off) + tile * ng * kTileN + r;
-    zptr[j] = a.zeros_off >= 0
-                  ? reinterpret_cast<const uint32_t*>(a.packed + a.zeros_off) + tile * ng * 2 + (r >> 3)
-                  : nullptr;
+    rb[j] = make_rsrc(a.packed + tile * ng * kUnitBytes, ng * kUnitBytes);
+    rs[j] = make_rsrc(a.packed + a.scales_off + tile * ng * (2 * kTileN), ng * 2 * kTileN);
+    rz[j] = make_rsrc(a.packed + (asym ? a.zeros_off : 0) + tile * ng * 8, ng * 8);
   }
+  const uint32_t lane_code = 16u * lane, lane_scale = 2u * r, lane_zero = 4u * (r >> 3);
 
   // X' staging: thread -> (row, 8-channel vector) pairs of the BM x 128 tile
   int a_row[A_VEC], a_col[A_VEC];
@@ -113,9 +113,9 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
-      breg[j] = bptr[j][static_cast<int64_t>(g) * 64];
-      sreg[j] = sptr[j][g * kTileN];
-      zreg[j] = zptr[j] ? zptr[j][g * 2] : 0u;
+      breg[j] = buf_load16(rb[j], lane_code, g * kUnitBytes);
+      sreg[j] = buf_load2(rs[j], lane_scale, g * (2 * kTileN));
+      zreg[j] = asym ? buf_load4(rz[j], lane_zero, g * 8) : 0u;
     }
   };
 
@@ -147,7 +147,7 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
       bcur[j] = breg[j];
-      const uint32_t z = zptr[j] ? (zreg[j] >> zshift) & 0xFu : 8u;
+      const uint32_t z = asym ? (zreg[j] >> zshift) & 0xFu : 8u;
       s2[j] = as_h2(sreg[j] | (sreg[j] << 16));
       nz1024[j] = neg_off1024(z);
       nz64[j] = neg_off64(z);

@@ -39,12 +39,17 @@ struct GemvArgs {
   int N, K, n_groups, phase_groups;
 };
 
-// X' for channels [k0, k0 + nk) of every row into xs[m][nk], then O and S for every
-// 32-channel slice into osum/ssum[m][nk / 32].
+// X' for channels [k0, k0 + nk) of every row into xs[m][nk], and O, S for every
+// 32-channel slice into osum/ssum[m][nk / 32]. A thread converts 8 channels; the 4
+// threads of a slice are consecutive lanes and add their partial sums with shuffles.
+// Channel k of a word has offset 1024 if k % 8 is in {0, 1, 4, 5}, else 64.
 template <int M, int NT>
 __device__ __forceinline__ void stage_phase(const GemvArgs& a, int k0, int nk, _Float16* xs,
                                             float* osum, float* ssum) {
-  const int vec_per_row = nk / 8;
+  const int vec_per_row = nk / 8;  // a multiple of 16
+  const half2_t one2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+  const half2_t o1024 = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
+  const half2_t o64 = {static_cast<_Float16>(64.0f), static_cast<_Float16>(64.0f)};
   for (int i = threadIdx.x; i < M * vec_per_row; i += NT) {
     const int m = i / vec_per_row, v = i - m * vec_per_row;
     uint4 val = *reinterpret_cast<const uint4*>(a.x + static_cast<int64_t>(m) * a.K + k0 + 8 * v);
@@ -64,26 +69,20 @@ __device__ __forceinline__ void stage_phase(const GemvArgs& a, int k0, int nk, _
       val = make_uint4(ow[0], ow[1], ow[2], ow[3]);
     }
     *reinterpret_cast<uint4*>(xs + m * nk + 8 * v) = val;
-  }
-  __syncthreads();
-  // 8 threads per slice, 4 channels each: channels 4j, 4j+1 have offset 1024 and
-  // 4j+2, 4j+3 offset 64 (positions k % 8 in {0,1,4,5} and {2,3,6,7})
-  const int slices = nk / 32;
-  for (int e8 = threadIdx.x; e8 < M * slices * 8; e8 += NT) {
-    const int e = e8 >> 3, j = e8 & 7;
-    const int m = e / slices, c = e - m * slices;
-    const uint2 xv = *reinterpret_cast<const uint2*>(xs + m * nk + c * 32 + 4 * j);
-    const half2_t lo = as_h2(xv.x), hi = as_h2(xv.y);
-    const float a01 = static_cast<float>(lo.x) + static_cast<float>(lo.y);
-    const float a23 = static_cast<float>(hi.x) + static_cast<float>(hi.y);
-    float sv = a01 + a23;
-    float ov = 1024.0f * a01 + 64.0f * a23;
-#pragma unroll
-    for (int o = 4; o > 0; o >>= 1) {
-      sv += __shfl_xor(sv, o, 8);
-      ov += __shfl_xor(ov, o, 8);
-    }
-    if (j == 0) {
+    float sv = __builtin_amdgcn_fdot2(as_h2(val.x), one2, 0.0f, false);
+    sv = __builtin_amdgcn_fdot2(as_h2(val.y), one2, sv, false);
+    sv = __builtin_amdgcn_fdot2(as_h2(val.z), one2, sv, false);
+    sv = __builtin_amdgcn_fdot2(as_h2(val.w), one2, sv, false);
+    float ov = __builtin_amdgcn_fdot2(as_h2(val.x), o1024, 0.0f, false);
+    ov = __builtin_amdgcn_fdot2(as_h2(val.y), o64, ov, false);
+    ov = __builtin_amdgcn_fdot2(as_h2(val.z), o1024, ov, false);
+    ov = __builtin_amdgcn_fdot2(as_h2(val.w), o64, ov, false);
+    sv += __shfl_xor(sv, 1, 4);
+    ov += __shfl_xor(ov, 1, 4);
+    sv += __shfl_xor(sv, 2, 4);
+    ov += __shfl_xor(ov, 2, 4);
+    if ((v & 3) == 0) {
+      const int e = m * (nk / 32) + (v >> 2);
       ssum[e] = sv;
       osum[e] = ov;
     }
@@ -96,7 +95,9 @@ __global__ void __launch_bounds__(WAVES * 64) gemv_kernel(GemvArgs a) {
   constexpr int NT = WAVES * 64;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int t = blockIdx.x;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wavefront index is uniform: keep it (and every group index) in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int r = lane & 15, p = lane >> 4;
   const int ng = a.n_groups;
 
@@ -105,91 +106,84 @@ __global__ void __launch_bounds__(WAVES * 64) gemv_kernel(GemvArgs a) {
   float* ssum = osum + M * a.phase_groups * 4;
   float* red = ssum + M * a.phase_groups * 4;  // [WAVES][M][16]
 
-  const uint4* codes = reinterpret_cast<const uint4*>(a.packed) + static_cast<int64_t>(t) * ng * 64 + lane;
-  const uint16_t* pscales =
-      reinterpret_cast<const uint16_t*>(a.packed + a.scales_off) + static_cast<int64_t>(t) * ng * kTileN + r;
-  const uint32_t* pzeros =
-      a.zeros_off >= 0
-          ? reinterpret_cast<const uint32_t*>(a.packed + a.zeros_off) + static_cast<int64_t>(t) * ng * 2 + (r >> 3)
-          : nullptr;
+  // buffer resources over this tile's codes, scales and zeros: the per-group offset is
+  // wavefront-uniform (SGPR), the per-lane offset constant (VGPR)
+  const __amdgpu_buffer_rsrc_t rcodes =
+      make_rsrc(a.packed + static_cast<int64_t>(t) * ng * kUnitBytes, ng * kUnitBytes);
+  const __amdgpu_buffer_rsrc_t rscales =
+      make_rsrc(a.packed + a.scales_off + static_cast<int64_t>(t) * ng * (2 * kTileN), ng * 2 * kTileN);
+  const bool asym = a.zeros_off >= 0;
+  const __amdgpu_buffer_rsrc_t rzeros =
+      make_rsrc(a.packed + (asym ? a.zeros_off : 0) + static_cast<int64_t>(t) * ng * 8, ng * 8);
+  const uint32_t lane_code = 16u * lane, lane_scale = 2u * r, lane_zero = 4u * (r >> 3);
   const int zshift = 4 * (r & 7);
 
   float yacc[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) yacc[m] = 0.0f;
 
+  struct Batch {
+    uint4 c[BATCH];
+    uint32_t s[BATCH], z[BATCH];
+  };
+  auto load = [&](Batch& b, int ph0, int jb, int nj) {
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      if (jb + u < nj) {
+        const uint32_t g = static_cast<uint32_t>(ph0 + wave + WAVES * (jb + u));
+        b.c[u] = buf_load16(rcodes, lane_code, g * kUnitBytes);
+        b.s[u] = buf_load2(rscales, lane_scale, g * (2 * kTileN));
+        b.z[u] = asym ? buf_load4(rzeros, lane_zero, g * 8) : 0u;
+      }
+    }
+  };
+  auto compute = [&](const Batch& b, int jb, int nj, int ngp, int nk) {
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      if (jb + u < nj) {
+        const int gl = wave + WAVES * (jb + u);
+        const _Float16* xg = xs + gl * kGroup + 32 * p;
+        float acc[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+        const uint32_t words[4] = {b.c[u].x, b.c[u].y, b.c[u].z, b.c[u].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const Pairs4 pr = unpack_word(words[i]);
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            const uint4 xv = *reinterpret_cast<const uint4*>(xg + m * nk + 8 * i);
+            acc[m] = __builtin_amdgcn_fdot2(as_h2(pr.p[0]), as_h2(xv.x), acc[m], false);
+            acc[m] = __builtin_amdgcn_fdot2(as_h2(pr.p[1]), as_h2(xv.y), acc[m], false);
+            acc[m] = __builtin_amdgcn_fdot2(as_h2(pr.p[2]), as_h2(xv.z), acc[m], false);
+            acc[m] = __builtin_amdgcn_fdot2(as_h2(pr.p[3]), as_h2(xv.w), acc[m], false);
+          }
+        }
+        const float s = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b.s[u])));
+        const float z = asym ? static_cast<float>((b.z[u] >> zshift) & 0xFu) : 8.0f;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const int e = (m * ngp + gl) * 4 + p;
+          yacc[m] += s * (acc[m] - osum[e] - z * ssum[e]);
+        }
+      }
+    }
+  };
+
   for (int ph0 = 0; ph0 < ng; ph0 += a.phase_groups) {
     const int ngp = min(a.phase_groups, ng - ph0);
     const int nk = ngp * kGroup;
     // this wavefront's groups in the phase: gl = wave + WAVES * j, j < nj
     const int nj = wave < ngp ? (ngp - wave + WAVES - 1) / WAVES : 0;
-
-    uint4 cw[BATCH];
-    uint32_t sb[BATCH], zw[BATCH];
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      cw[u] = make_uint4(0, 0, 0, 0);
-      sb[u] = zw[u] = 0;
-      if (u < nj) {
-        const int g = ph0 + wave + WAVES * u;
-        cw[u] = codes[static_cast<int64_t>(g) * 64];
-        sb[u] = pscales[g * kTileN];
-        zw[u] = pzeros ? pzeros[g * 2] : 0u;
-      }
-    }
+    Batch b0, b1;
+    load(b0, ph0, 0, nj);
     if (ph0 != 0) __syncthreads();  // the previous phase is done with LDS
     stage_phase<M, NT>(a, ph0 * kGroup, nk, xs, osum, ssum);
-
-    for (int jb = 0; jb < nj; jb += BATCH) {
-      uint4 cn[BATCH];
-      uint32_t sn[BATCH], zn[BATCH];
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        cn[u] = make_uint4(0, 0, 0, 0);
-        sn[u] = zn[u] = 0;
-        if (jb + BATCH + u < nj) {
-          const int g = ph0 + wave + WAVES * (jb + BATCH + u);
-          cn[u] = codes[static_cast<int64_t>(g) * 64];
-          sn[u] = pscales[g * kTileN];
-          zn[u] = pzeros ? pzeros[g * 2] : 0u;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        if (jb + u < nj) {
-          const int gl = wave + WAVES * (jb + u);
-          const _Float16* xg = xs + gl * kGroup + 32 * p;
-          float acc[M];
-#pragma unroll
-          for (int m = 0; m < M; ++m) acc[m] = 0.0f;
-          const uint32_t words[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const Pairs4 pr = unpack_word(words[i]);
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-              const uint4 xv = *reinterpret_cast<const uint4*>(xg + m * nk + 8 * i);
-              acc[m] = __builtin_amdgcn_fdot2(as_h2(pr.p[0]), as_h2(xv.x), acc[m], false);
-              acc[m] = __builtin_amdgcn_fdot2(as_h2(pr.p[1]), as_h2(xv.y), acc[m], false);
-              acc[m] = __builtin_amdgcn_fdot2(as_h2(pr.p[2]), as_h2(xv.z), acc[m], false);
-              acc[m] = __builtin_amdgcn_fdot2(as_h2(pr.p[3]), as_h2(xv.w), acc[m], false);
-            }
-          }
-          const float s = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(sb[u])));
-          const float z = pzeros ? static_cast<float>((zw[u] >> zshift) & 0xFu) : 8.0f;
-#pragma unroll
-          for (int m = 0; m < M; ++m) {
-            const int e = (m * ngp + gl) * 4 + p;
-            yacc[m] += s * (acc[m] - osum[e] - z * ssum[e]);
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        cw[u] = cn[u];
-        sb[u] = sn[u];
-        zw[u] = zn[u];
-      }
+    for (int jb = 0; jb < nj; jb += 2 * BATCH) {
+      load(b1, ph0, jb + BATCH, nj);
+      compute(b0, jb, nj, ngp, nk);
+      load(b0, ph0, jb + 2 * BATCH, nj);
+      compute(b1, jb + BATCH, nj, ngp, nk);
     }
   }
 
@@ -214,8 +208,11 @@ __global__ void __launch_bounds__(WAVES * 64) gemv_kernel(GemvArgs a) {
   }
 }
 
-constexpr int kWavesDefault = 8;
-constexpr int kBatchDefault = 4;
+// Two groups in flight per wavefront per batch (double-buffered), and 16 wavefronts per
+// workgroup when there are few tiles (N <= 8192: one workgroup per CU, more loads in
+// flight per CU), 8 otherwise (several workgroups per CU).
+constexpr int kBatchDefault = 2;
+inline bool many_waves(int64_t n_tiles) { return n_tiles <= 512; }
 
 int phase_groups_for(int M, int n_groups) {
   int pg = kLdsBudget / (M * (2 * kGroup + 32));
@@ -236,6 +233,12 @@ hipError_t launch_cfg(const GemvArgs& a, int64_t n_tiles, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int M>
+hipError_t launch_m(const GemvArgs& a, int64_t n_tiles, hipStream_t st) {
+  if (many_waves(n_tiles)) return launch_cfg<M, 16, kBatchDefault>(a, n_tiles, st);
+  return launch_cfg<M, 8, kBatchDefault>(a, n_tiles, st);
+}
+
 // Tuning override for sweeps (M = 1 only): AWQ_GEMV_CFG = "waves,batch".
 hipError_t launch_m1(const GemvArgs& a, int64_t n_tiles, hipStream_t st) {
   const char* env = getenv("AWQ_GEMV_CFG");
@@ -243,14 +246,15 @@ hipError_t launch_m1(const GemvArgs& a, int64_t n_tiles, hipStream_t st) {
     int w = 0, b = 0;
     if (sscanf(env, "%d,%d", &w, &b) == 2) {
       if (w == 4 && b == 4) return launch_cfg<1, 4, 4>(a, n_tiles, st);
-      if (w == 4 && b == 8) return launch_cfg<1, 4, 8>(a, n_tiles, st);
+      if (w == 8 && b == 1) return launch_cfg<1, 8, 1>(a, n_tiles, st);
       if (w == 8 && b == 2) return launch_cfg<1, 8, 2>(a, n_tiles, st);
-      if (w == 8 && b == 8) return launch_cfg<1, 8, 8>(a, n_tiles, st);
+      if (w == 8 && b == 4) return launch_cfg<1, 8, 4>(a, n_tiles, st);
+      if (w == 16 && b == 1) return launch_cfg<1, 16, 1>(a, n_tiles, st);
       if (w == 16 && b == 2) return launch_cfg<1, 16, 2>(a, n_tiles, st);
       if (w == 16 && b == 4) return launch_cfg<1, 16, 4>(a, n_tiles, st);
     }
   }
-  return launch_cfg<1, kWavesDefault, kBatchDefault>(a, n_tiles, st);
+  return launch_m<1>(a, n_tiles, st);
 }
 
 }  // namespace
@@ -274,13 +278,13 @@ hipError_t launch_gemv(const uint16_t* x, const uint16_t* inv_s_c, const void* p
   a.phase_groups = phase_groups_for(static_cast<int>(M), a.n_groups);
   switch (M) {
     case 1: return launch_m1(a, L.n_tiles, st);
-    case 2: return launch_cfg<2, kWavesDefault, kBatchDefault>(a, L.n_tiles, st);
-    case 3: return launch_cfg<3, kWavesDefault, kBatchDefault>(a, L.n_tiles, st);
-    case 4: return launch_cfg<4, kWavesDefault, kBatchDefault>(a, L.n_tiles, st);
-    case 5: return launch_cfg<5, kWavesDefault, 2>(a, L.n_tiles, st);
-    case 6: return launch_cfg<6, kWavesDefault, 2>(a, L.n_tiles, st);
-    case 7: return launch_cfg<7, kWavesDefault, 2>(a, L.n_tiles, st);
-    case 8: return launch_cfg<8, kWavesDefault, 2>(a, L.n_tiles, st);
+    case 2: return launch_m<2>(a, L.n_tiles, st);
+    case 3: return launch_m<3>(a, L.n_tiles, st);
+    case 4: return launch_m<4>(a, L.n_tiles, st);
+    case 5: return launch_m<5>(a, L.n_tiles, st);
+    case 6: return launch_m<6>(a, L.n_tiles, st);
+    case 7: return launch_m<7>(a, L.n_tiles, st);
+    case 8: return launch_m<8>(a, L.n_tiles, st);
     default: return hipErrorInvalidValue;
   }
 }
