@@ -140,29 +140,36 @@ def main():
     value_gbs = step_bytes * K / sec / 1e9
 
     # ------------------------------------------- per-kernel durations (HIP events)
-    # The launches are queued behind a GPU sleep so that the events bracket back-to-back
-    # kernel execution, not host launch latency.
-    n_kt = min(K, 4 * rot)
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in layers] for _ in range(n_kt)]
-    torch.cuda.synchronize()
-    torch.cuda._sleep(int(1e8))
-    for s in range(n_kt):
-        run_step(s % rot, ev[s])
-    torch.cuda.synchronize()
-    dur_us = {L["name"]: [] for L in layers}
-    for s in range(n_kt):
-        for j, L in enumerate(layers):
-            dur_us[L["name"]].append(ev[s][j][0].elapsed_time(ev[s][j][1]) * 1e3)
+    # One graph per layer shape holding that layer's GEMV over all its weight copies,
+    # replayed between two events on the capture stream: launches run back to back, and
+    # the average per launch is the kernel time (checked against rocprofv3's trace).
     per_layer = {}
-    for L in layers:
-        avg = float(np.mean(dur_us[L["name"]]))
-        per_layer[L["name"]] = {"shape": f"{L['k']}->{L['n']}", "us": round(avg, 3),
-                                "GB/s": round(L["bytes"] / avg / 1e3, 1)}
+    for shape_layer in ("q", "gate", "down"):
+        j = next(i for i, L in enumerate(layers) if L["name"] == shape_layer)
+        L = layers[j]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(rot):
+                awq.awq_gemv(L["x"], L["inv"], copies[j][r], L["n"], L["k"], GROUP,
+                             awq.FMT_ASYM, y=L["y"], ws=ws)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(2, (8 * K) // (7 * rot))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * rot)
+        per_layer[shape_layer] = {"shape": f"{L['k']}->{L['n']}", "us": round(us, 3),
+                                  "GB/s": round(L["bytes"] / us / 1e3, 1), "launches": reps * rot}
+        del g
     dom = next(L for L in layers if L["name"] == DOMINANT)
     dom_us = per_layer[DOMINANT]["us"]
     achieved = dom["bytes"] / dom_us / 1e3  # GB/s
-    sum_kernel_us = sum(v["us"] for v in per_layer.values())
+    sum_kernel_us = 4 * per_layer["q"]["us"] + 2 * per_layer["gate"]["us"] + per_layer["down"]["us"]
+    traffic = measured_traffic(dom["bytes"])
 
     # ------------------------------------------------------------ prefill GEMM
     gemm = None
@@ -238,7 +245,7 @@ def main():
                    "submission": "one HIP graph per step"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
                      "peak": rl.HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / rl.HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / rl.HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": f"awq_gemv 4096->11008 M=1 ({dom_us:.3f} us/launch)"},
         "per_layer_kernel": per_layer,
         "kernel_sum_us_per_step": round(sum_kernel_us, 3),
@@ -247,6 +254,38 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_4096x11008_m1_traffic.txt")
+GEMV_SOURCES = ("bit_weight_only_w4a16_amd/csrc/gemv.hip",
+                "bit_weight_only_w4a16_amd/csrc/awq_internal.hpp")
+
+
+def gemv_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMV_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(algorithmic_bytes: int):
+    """HBM bytes per launch of the dominant GEMV, as measured by rocprofv3 counters
+    (FETCH_SIZE + WRITE_SIZE, each scaled by what it reads for a plain copy of known
+    size) and recorded with the hash of the kernel source; None if the kernel source
+    changed since, or if no measurement is recorded."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != gemv_source_hash():
+        return None
+    return int(float(kv["traffic_bytes_per_launch"]))
 
 
 def cpu_baseline(seconds: float):

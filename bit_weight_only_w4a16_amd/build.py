@@ -40,9 +40,17 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the ROCm toolchain is required to build the library")
 
 
+# Matrix-core kernels keep their float32 accumulators in ordinary VGPRs: with AGPRs the
+# register allocator copies accumulators between AGPRs inside the main loop.
+FILE_FLAGS = {
+    "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gemm_lds.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -61,6 +61,9 @@ hipError_t launch_gemv(const uint16_t* x, const uint16_t* inv_s_c, const void* p
                        int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y, void* ws,
                        size_t ws_bytes, hipStream_t st);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_lds(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
+                           int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y, int cfg,
+                           hipStream_t st);
 hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
                        int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y, void* ws,
                        size_t ws_bytes, hipStream_t st);
@@ -69,20 +72,26 @@ hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* p
 // Buffer resource over [base, base + bytes): loads take a wavefront-uniform SGPR offset
 // plus a per-lane VGPR offset, so streaming through the weights costs no 64-bit address
 // arithmetic; an offset past `bytes` reads 0. Word 3 is the gfx9 raw-buffer format.
+// The SGPR offset goes through readfirstlane: callers pass uniform values, and this
+// keeps the compiler from treating them as divergent (which would wrap every load in
+// a scalarisation loop).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
                                            0x00020000);
 }
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   typedef unsigned int u4 __attribute__((ext_vector_type(4)));
-  const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), 0);
+  const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff),
+                                              __builtin_amdgcn_readfirstlane(static_cast<int>(soff)), 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(voff), static_cast<int>(soff), 0);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(voff),
+                                              __builtin_amdgcn_readfirstlane(static_cast<int>(soff)), 0);
 }
 __device__ __forceinline__ uint32_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(voff), static_cast<int>(soff), 0);
+  return __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(voff),
+                                              __builtin_amdgcn_readfirstlane(static_cast<int>(soff)), 0);
 }
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));

@@ -10,14 +10,20 @@
 //  * v_mfma_f32_16x16x32_f16: lane l feeds row/column l % 16 and k slots 8 (l / 16)..+7.
 //    In the gfx950 layout a lane's 16 bytes of a unit are row l % 16, channels
 //    32 (l / 16) + 8 i + 0..7 for word i, so word i is exactly the B operand of k-step i
-//    of the group (the slots of step i stand for channels 32 j + 8 i + e, j = l / 16): one
-//    128-bit global load per lane gives the B operands of a 16-row tile for a whole
-//    group, with no LDS round trip. The X' operand uses the same slot-to-channel map.
-//  * X' tiles (binary16(X * inv_s_c)) are staged in LDS one group (128 channels) at a
-//    time, rows padded by 16 bytes; the next group's X' and weights are loaded into
-//    registers while the current group is multiplied.
+//    of the group (the slots of step i stand for channels 32 j + 8 i + e, j = l / 16):
+//    one 128-bit buffer load per lane gives the B operands of a 16-row weight tile for
+//    a whole group, with no LDS round trip. The X' operand uses the same slot map.
+//  * X' (binary16(X * inv_s_c)) goes through LDS, one 128-channel group per stage,
+//    double-buffered: while group g is multiplied from one buffer, group g + 1 is
+//    written to the other from registers loaded a stage earlier, and group g + 2 is
+//    being fetched from memory; one barrier per group. Rows are padded by 16 bytes so
+//    the 16 rows read by one instruction fall in distinct LDS banks.
+//  * The weights of group g + 1 are in registers while group g is multiplied.
 //  * Four wavefronts per workgroup in a 2 x 2 arrangement; each computes WM x WN
-//    matrix-core tiles of 16 x 16.
+//    matrix-core tiles of 16 x 16 (up to 128 x 64 outputs, accumulators in AGPRs), so
+//    one dequantized weight fragment feeds WM instructions.
+//  * Workgroups are numbered so that the ones a given XCD (L2 slice) runs are
+//    neighbours along M: they share the same weight columns in that L2.
 #include "awq_internal.hpp"
 
 #include <stdio.h>
@@ -28,6 +34,7 @@ namespace {
 
 constexpr int kLdsStride = kGroup + 8;  // halfs per LDS row (16-byte pad)
 constexpr int kGThreads = 256;
+constexpr int kXcds = 8;
 
 struct GemmArgs {
   const uint16_t* x;
@@ -36,86 +43,101 @@ struct GemmArgs {
   uint16_t* y;
   int64_t scales_off;
   int64_t zeros_off;
+  uint32_t packed_bytes;
   int M, N, K, n_groups, n_tiles, n_blocks_n, n_blocks_m;
 };
 
 __device__ __forceinline__ uint4 scale_x(uint4 val, uint4 iv) {
-  const uint32_t xw[4] = {val.x, val.y, val.z, val.w};
-  const uint32_t iw[4] = {iv.x, iv.y, iv.z, iv.w};
-  uint32_t ow[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const half2_t xh = as_h2(xw[j]), ih = as_h2(iw[j]);
-    half2_t rr;
-    rr.x = static_cast<_Float16>(static_cast<float>(xh.x) * static_cast<float>(ih.x));
-    rr.y = static_cast<_Float16>(static_cast<float>(xh.y) * static_cast<float>(ih.y));
-    ow[j] = as_u32(rr);
-  }
-  return make_uint4(ow[0], ow[1], ow[2], ow[3]);
+  // binary16(x * inv): the product of two binary16 values is exact before the rounding
+  const half2_t a0 = as_h2(val.x) * as_h2(iv.x), a1 = as_h2(val.y) * as_h2(iv.y);
+  const half2_t a2 = as_h2(val.z) * as_h2(iv.z), a3 = as_h2(val.w) * as_h2(iv.w);
+  return make_uint4(as_u32(a0), as_u32(a1), as_u32(a2), as_u32(a3));
 }
 
-template <int WM, int WN>
+// SCHED > 0: ask the scheduler to issue each matrix instruction followed by SCHED VALU
+// instructions (and an LDS read every WN of them), so that the dequantization of the
+// next weight fragments runs while the matrix core is busy.
+template <int WAVES_M, int WM, int WN, int SCHED>
 __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
-  constexpr int BM = 2 * WM * 16, BN = 2 * WN * 16;
+  constexpr int WAVES_N = 4 / WAVES_M;
+  constexpr int BM = WAVES_M * WM * 16, BN = WAVES_N * WN * 16;
   constexpr int A_VEC = BM * (kGroup / 8) / kGThreads;  // 16-byte X' vectors per thread
-  __shared__ __attribute__((aligned(16))) _Float16 xs[BM * kLdsStride];
+  constexpr int BUF = BM * kLdsStride;                  // halfs per LDS buffer
+  extern __shared__ __attribute__((aligned(16))) _Float16 xs[];  // [2][BM][kLdsStride]
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
   const int lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int r = lane & 15, p = lane >> 4;
 
-  // workgroup -> output block; consecutive workgroups walk down M first so that the
-  // ones running together share their weight tiles in L2
-  const int bid = blockIdx.x;
+  // workgroup -> output block. Blocks are dealt to the XCDs round-robin; renumber so
+  // that each XCD gets a contiguous run, walked down M first (shared weight columns).
+  const int nb = a.n_blocks_m * a.n_blocks_n;
+  int bid = blockIdx.x;
+  if (nb % kXcds == 0) bid = (bid % kXcds) * (nb / kXcds) + bid / kXcds;
   const int bm = bid % a.n_blocks_m, bn = bid / a.n_blocks_m;
   const int m_blk = bm * BM, n_blk = bn * BN;
   const int ng = a.n_groups;
 
-  // this wavefront's weight tiles (clamped: tiles past the last one are read but their
-  // rows are >= N and never stored), as buffer resources: the per-group offset is
-  // uniform (SGPR), the per-lane offset constant
-  __amdgpu_buffer_rsrc_t rb[WN], rs[WN], rz[WN];
+  // one buffer resource over the whole packed layer; this wavefront's weight tiles are
+  // addressed by wavefront-uniform (SGPR) offsets (tiles past the last one are clamped:
+  // their rows are >= N and never stored). Few SGPRs: no resource ends up in VGPRs.
   const bool asym = a.zeros_off >= 0;
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.packed, a.packed_bytes);
+  uint32_t code_off[WN], scale_off[WN], zero_off[WN];
 #pragma unroll
   for (int j = 0; j < WN; ++j) {
-    const int64_t tile = min(n_blk / kTileN + wn * WN + j, a.n_tiles - 1);
-    rb[j] = make_rsrc(a.packed + tile * ng * kUnitBytes, ng * kUnitBytes);
-    rs[j] = make_rsrc(a.packed + a.scales_off + tile * ng * (2 * kTileN), ng * 2 * kTileN);
-    rz[j] = make_rsrc(a.packed + (asym ? a.zeros_off : 0) + tile * ng * 8, ng * 8);
+    const uint32_t tile = static_cast<uint32_t>(min(n_blk / kTileN + wn * WN + j, a.n_tiles - 1));
+    code_off[j] = tile * ng * kUnitBytes;
+    scale_off[j] = static_cast<uint32_t>(a.scales_off) + tile * ng * (2 * kTileN);
+    zero_off[j] = asym ? static_cast<uint32_t>(a.zeros_off) + tile * ng * 8 : 0u;
   }
   const uint32_t lane_code = 16u * lane, lane_scale = 2u * r, lane_zero = 4u * (r >> 3);
+  const int zshift = 4 * (r & 7);
 
-  // X' staging: thread -> (row, 8-channel vector) pairs of the BM x 128 tile
-  int a_row[A_VEC], a_col[A_VEC];
-  bool a_ok[A_VEC];
+  // X' rows of this block as one buffer resource (rows past M read as 0)
+  const int rows_here = min(BM, a.M - m_blk);
+  const __amdgpu_buffer_rsrc_t rx =
+      make_rsrc(a.x + static_cast<int64_t>(m_blk) * a.K, static_cast<uint32_t>(rows_here) * a.K * 2);
+  uint32_t a_voff[A_VEC];
+  int a_lds[A_VEC], a_col[A_VEC];
 #pragma unroll
   for (int it = 0; it < A_VEC; ++it) {
     const int v = threadIdx.x + it * kGThreads;
-    a_row[it] = v >> 4;
-    a_col[it] = (v & 15) * 8;
-    a_ok[it] = m_blk + a_row[it] < a.M;
+    const int row = v >> 4, col = (v & 15) * 8;
+    a_voff[it] = static_cast<uint32_t>(row * a.K + col) * 2;
+    a_lds[it] = row * kLdsStride + col;
+    a_col[it] = col;
   }
-  const uint16_t* xrow[A_VEC];
-#pragma unroll
-  for (int it = 0; it < A_VEC; ++it)
-    xrow[it] = a.x + static_cast<int64_t>(a_ok[it] ? m_blk + a_row[it] : 0) * a.K + a_col[it];
 
   uint4 areg[A_VEC];
-  uint4 breg[WN];
-  uint32_t sreg[WN], zreg[WN];
-
-  auto load_group = [&](int g) {
+  auto load_a = [&](int g) {
 #pragma unroll
-    for (int it = 0; it < A_VEC; ++it) {
-      areg[it] = a_ok[it] ? *reinterpret_cast<const uint4*>(xrow[it] + g * kGroup)
-                          : make_uint4(0, 0, 0, 0);
+    for (int it = 0; it < A_VEC; ++it) areg[it] = buf_load16(rx, a_voff[it], g * kGroup * 2);
+  };
+  auto store_a = [&](int g, int buf) {
+    _Float16* dst = xs + buf * BUF;
+    if (a.inv) {
+#pragma unroll
+      for (int it = 0; it < A_VEC; ++it) {
+        const uint4 iv = *reinterpret_cast<const uint4*>(a.inv + g * kGroup + a_col[it]);
+        *reinterpret_cast<uint4*>(dst + a_lds[it]) = scale_x(areg[it], iv);
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < A_VEC; ++it) *reinterpret_cast<uint4*>(dst + a_lds[it]) = areg[it];
     }
+  };
+  struct BRegs {
+    uint4 c[WN];
+    uint32_t s[WN], z[WN];
+  };
+  auto load_b = [&](BRegs& b, int g) {
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
-      breg[j] = buf_load16(rb[j], lane_code, g * kUnitBytes);
-      sreg[j] = buf_load2(rs[j], lane_scale, g * (2 * kTileN));
-      zreg[j] = asym ? buf_load4(rz[j], lane_zero, g * 8) : 0u;
+      b.c[j] = buf_load16(rp, lane_code, code_off[j] + g * kUnitBytes);
+      b.s[j] = buf_load2(rp, lane_scale, scale_off[j] + g * (2 * kTileN));
+      b.z[j] = asym ? buf_load4(rp, lane_zero, zero_off[j] + g * 8) : 0u;
     }
   };
 
@@ -125,42 +147,23 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[i][j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  load_group(0);
-  const int zshift = 4 * (r & 7);
-  for (int g = 0; g < ng; ++g) {
-    // X' of group g into LDS (scaled by inv_s_c), weights of group g into the B registers
-    uint4 iv[A_VEC];
-    if (a.inv) {
-#pragma unroll
-      for (int it = 0; it < A_VEC; ++it)
-        iv[it] = *reinterpret_cast<const uint4*>(a.inv + g * kGroup + a_col[it]);
-    }
-    __syncthreads();  // everyone is done reading the previous group's tile
-#pragma unroll
-    for (int it = 0; it < A_VEC; ++it) {
-      const uint4 val = a.inv ? scale_x(areg[it], iv[it]) : areg[it];
-      *reinterpret_cast<uint4*>(&xs[a_row[it] * kLdsStride + a_col[it]]) = val;
-    }
-    uint4 bcur[WN];
+  auto compute = [&](const BRegs& b, int buf) {
+    const _Float16* src = xs + buf * BUF;
     half2_t s2[WN];
     uint32_t nz1024[WN], nz64[WN];
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
-      bcur[j] = breg[j];
-      const uint32_t z = asym ? (zreg[j] >> zshift) & 0xFu : 8u;
-      s2[j] = as_h2(sreg[j] | (sreg[j] << 16));
+      const uint32_t z = asym ? (b.z[j] >> zshift) & 0xFu : 8u;
+      s2[j] = as_h2(b.s[j] | (b.s[j] << 16));
       nz1024[j] = neg_off1024(z);
       nz64[j] = neg_off64(z);
     }
-    __syncthreads();
-    if (g + 1 < ng) load_group(g + 1);
-
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       half8_t bf[WN];
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
-        const uint32_t w = i == 0 ? bcur[j].x : i == 1 ? bcur[j].y : i == 2 ? bcur[j].z : bcur[j].w;
+        const uint32_t w = i == 0 ? b.c[j].x : i == 1 ? b.c[j].y : i == 2 ? b.c[j].z : b.c[j].w;
         half2_t d[4];
         dequant_word(w, nz1024[j], nz64[j], s2[j], d);
         bf[j] = half8_t{d[0].x, d[0].y, d[1].x, d[1].y, d[2].x, d[2].y, d[3].x, d[3].y};
@@ -168,15 +171,49 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int ms = 0; ms < WM; ++ms) {
         const int row = wm * WM * 16 + ms * 16 + r;
-        const half8_t af =
-            *reinterpret_cast<const half8_t*>(&xs[row * kLdsStride + 32 * p + 8 * i]);
+        const half8_t af = *reinterpret_cast<const half8_t*>(src + row * kLdsStride + 32 * p + 8 * i);
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
           acc[ms][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[j], acc[ms][j], 0, 0, 0);
         }
       }
     }
+    if constexpr (SCHED > 0) {
+#pragma unroll
+      for (int q = 0; q < 4 * WM * WN; ++q) {
+        if (q % WN == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, SCHED, 0);               // VALU
+      }
+    }
+  };
+
+  // prologue: X'(0) in LDS buffer 0, X'(1) and B(0) in registers
+  BRegs b0, b1;
+  load_a(0);
+  load_b(b0, 0);
+  store_a(0, 0);
+  if (ng > 1) load_a(1);
+  __syncthreads();
+
+  int g = 0;
+  for (; g + 1 < ng; g += 2) {
+    // even group: compute from buffer 0 with b0; prefetch B(g+1); stage X'(g+1)
+    load_b(b1, g + 1);
+    compute(b0, 0);
+    store_a(g + 1, 1);
+    if (g + 2 < ng) load_a(g + 2);
+    __syncthreads();
+    // odd group: compute from buffer 1 with b1
+    if (g + 2 < ng) load_b(b0, g + 2);
+    compute(b1, 1);
+    if (g + 2 < ng) {
+      store_a(g + 2, 0);
+      if (g + 3 < ng) load_a(g + 3);
+    }
+    __syncthreads();
   }
+  if (g < ng) compute(b0, 0);  // odd number of groups: the last one is in buffer 0
 
   // epilogue: element q of acc[ms][j] is row 4 (l / 16) + q, column l % 16 of its tile
 #pragma unroll
@@ -196,13 +233,22 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
   }
 }
 
-template <int WM, int WN>
+template <int WAVES_M, int WM, int WN, int SCHED = 0>
 hipError_t launch_tiles(GemmArgs a, hipStream_t st) {
-  constexpr int BM = 2 * WM * 16, BN = 2 * WN * 16;
+  constexpr int BM = WAVES_M * WM * 16, BN = (4 / WAVES_M) * WN * 16;
+  const size_t lds = 2ull * BM * kLdsStride * sizeof(_Float16);
+  static bool attr_set = false;  // benign race: every thread sets the same value
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<WAVES_M, WM, WN, SCHED>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
   a.n_blocks_m = (a.M + BM - 1) / BM;
   a.n_blocks_n = (a.N + BN - 1) / BN;
   const unsigned blocks = static_cast<unsigned>(a.n_blocks_m) * static_cast<unsigned>(a.n_blocks_n);
-  hipLaunchKernelGGL((gemm_kernel<WM, WN>), dim3(blocks), dim3(kGThreads), 0, st, a);
+  hipLaunchKernelGGL((gemm_kernel<WAVES_M, WM, WN, SCHED>), dim3(blocks), dim3(kGThreads), lds, st, a);
   return hipGetLastError();
 }
 
@@ -221,21 +267,39 @@ hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* p
   a.y = y;
   a.scales_off = L.scales_off;
   a.zeros_off = L.zeros_off;
+  a.packed_bytes = static_cast<uint32_t>(L.total_bytes);
   a.M = static_cast<int>(M);
   a.N = static_cast<int>(N);
   a.K = static_cast<int>(K);
   a.n_groups = static_cast<int>(L.n_groups);
   a.n_tiles = static_cast<int>(L.n_tiles);
+  // AWQ_GEMM_TILE = "lds,<WM*10+WN>" selects the LDS-dequant kernel,
+  // "waves_m,wm,wn,sched" a register-fed tiling (for tuning sweeps)
   const char* env = getenv("AWQ_GEMM_TILE");
-  int wm = 0, wn = 0;
-  if (env && sscanf(env, "%d,%d", &wm, &wn) == 2) {
-    if (wm == 2 && wn == 2) return launch_tiles<2, 2>(a, st);
-    if (wm == 4 && wn == 2) return launch_tiles<4, 2>(a, st);
-    if (wm == 4 && wn == 4) return launch_tiles<4, 4>(a, st);
+  int lcfg = 0;
+  if (env && sscanf(env, "lds,%d", &lcfg) == 1)
+    return launch_gemm_lds(x, inv_s_c, packed, M, N, K, fmt, y, lcfg, st);
+  int wv = 0, wm = 0, wn = 0, sc = 0;
+  if (env && sscanf(env, "%d,%d,%d,%d", &wv, &wm, &wn, &sc) == 4) {
+    if (wv == 1 && wm == 4 && wn == 4 && sc == 0) return launch_tiles<1, 4, 4, 0>(a, st);
+    if (wv == 1 && wm == 4 && wn == 4 && sc == 2) return launch_tiles<1, 4, 4, 2>(a, st);
+    if (wv == 1 && wm == 4 && wn == 4 && sc == 3) return launch_tiles<1, 4, 4, 3>(a, st);
+    if (wv == 1 && wm == 4 && wn == 4 && sc == 4) return launch_tiles<1, 4, 4, 4>(a, st);
+    if (wv == 1 && wm == 8 && wn == 4 && sc == 0) return launch_tiles<1, 8, 4, 0>(a, st);
+    if (wv == 1 && wm == 8 && wn == 4 && sc == 2) return launch_tiles<1, 8, 4, 2>(a, st);
+    if (wv == 1 && wm == 8 && wn == 2 && sc == 0) return launch_tiles<1, 8, 2, 0>(a, st);
+    if (wv == 1 && wm == 8 && wn == 2 && sc == 3) return launch_tiles<1, 8, 2, 3>(a, st);
+    if (wv == 1 && wm == 4 && wn == 2 && sc == 0) return launch_tiles<1, 4, 2, 0>(a, st);
+    if (wv == 1 && wm == 4 && wn == 8 && sc == 0) return launch_tiles<1, 4, 8, 0>(a, st);
+    if (wv == 2 && wm == 4 && wn == 4 && sc == 0) return launch_tiles<2, 4, 4, 0>(a, st);
+    if (wv == 1 && wm == 2 && wn == 4 && sc == 0) return launch_tiles<1, 2, 4, 0>(a, st);
+    if (wv == 1 && wm == 1 && wn == 4 && sc == 0) return launch_tiles<1, 1, 4, 0>(a, st);
   }
-  if (M <= 32) return launch_tiles<1, 4>(a, st);
-  if (M <= 64) return launch_tiles<2, 4>(a, st);
-  return launch_tiles<4, 4>(a, st);
+  // Defaults from sweeps on MI355X: at M <= 64 the product is bound by streaming the
+  // weights, and narrow 64 x 128 workgroup tiles give the most workgroups; at larger M a
+  // 64 x 256 tile (each wavefront 64 x 64) runs best.
+  if (M <= 64) return launch_tiles<1, 4, 2>(a, st);
+  return launch_tiles<1, 4, 4>(a, st);
 }
 
 }  // namespace awq
