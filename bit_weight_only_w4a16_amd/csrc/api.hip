@@ -18,7 +18,7 @@ int check_shape(int64_t N, int64_t K, int32_t group, int32_t fmt) {
   if (fmt != AWQ_FMT_ASYM && fmt != AWQ_FMT_SYM8) return AWQ_ERR_INVALID_ARG;
   if (N % 8 != 0 || K % 8 != 0 || K % group != 0) return AWQ_ERR_INVALID_ARG;
   if (group != kGroup) return AWQ_ERR_UNSUPPORTED;
-  if (N * K >= (int64_t{1} << 32) || N >= (int64_t{1} << 30) || K > (int64_t{1} << 22))
+  if (N * K >= (int64_t{1} << 31) || N >= (int64_t{1} << 30) || K > (int64_t{1} << 22))
     return AWQ_ERR_UNSUPPORTED;
   return AWQ_OK;
 }

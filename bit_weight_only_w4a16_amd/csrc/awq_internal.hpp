@@ -75,6 +75,11 @@ hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* p
 // The SGPR offset goes through readfirstlane: callers pass uniform values, and this
 // keeps the compiler from treating them as divergent (which would wrap every load in
 // a scalarisation loop).
+// Per-lane offset that lies past the end of every buffer resource used here (each covers
+// less than 2^31 bytes: the entry points reject larger layers), so a load given it
+// returns zeros without a memory access. Loads use it instead of a branch.
+constexpr uint32_t kNoLoad = 0x80000000u;
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
                                            0x00020000);

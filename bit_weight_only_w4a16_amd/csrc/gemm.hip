@@ -18,10 +18,13 @@
 //    written to the other from registers loaded a stage earlier, and group g + 2 is
 //    being fetched from memory; one barrier per group. Rows are padded by 16 bytes so
 //    the 16 rows read by one instruction fall in distinct LDS banks.
-//  * The weights of group g + 1 are in registers while group g is multiplied.
-//  * Four wavefronts per workgroup in a 2 x 2 arrangement; each computes WM x WN
-//    matrix-core tiles of 16 x 16 (up to 128 x 64 outputs, accumulators in AGPRs), so
-//    one dequantized weight fragment feeds WM instructions.
+//  * The weights of group g + 1 are in registers while group g is multiplied. Every
+//    load is issued unconditionally (a group past the end reads zeros through an
+//    out-of-range lane offset), so the compiler's wait counts cover exactly the loads
+//    each step needs and never drain the prefetches behind them.
+//  * Four wavefronts per workgroup, side by side along N (or 2 x 2); each computes
+//    WM x WN matrix-core tiles of 16 x 16 (up to 128 x 64 outputs, accumulators in
+//    VGPRs), so one dequantized weight fragment feeds WM instructions.
 //  * Workgroups are numbered so that the ones a given XCD (L2 slice) runs are
 //    neighbours along M: they share the same weight columns in that L2.
 #include "awq_internal.hpp"
@@ -57,7 +60,7 @@ __device__ __forceinline__ uint4 scale_x(uint4 val, uint4 iv) {
 // SCHED > 0: ask the scheduler to issue each matrix instruction followed by SCHED VALU
 // instructions (and an LDS read every WN of them), so that the dequantization of the
 // next weight fragments runs while the matrix core is busy.
-template <int WAVES_M, int WM, int WN, int SCHED>
+template <int WAVES_M, int WM, int WN, int SCHED, bool ASYM>
 __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int BM = WAVES_M * WM * 16, BN = WAVES_N * WN * 16;
@@ -78,11 +81,11 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
   const int bm = bid % a.n_blocks_m, bn = bid / a.n_blocks_m;
   const int m_blk = bm * BM, n_blk = bn * BN;
   const int ng = a.n_groups;
+  const bool has_inv = a.inv != nullptr;
 
   // one buffer resource over the whole packed layer; this wavefront's weight tiles are
   // addressed by wavefront-uniform (SGPR) offsets (tiles past the last one are clamped:
   // their rows are >= N and never stored). Few SGPRs: no resource ends up in VGPRs.
-  const bool asym = a.zeros_off >= 0;
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.packed, a.packed_bytes);
   uint32_t code_off[WN], scale_off[WN], zero_off[WN];
 #pragma unroll
@@ -90,54 +93,64 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
     const uint32_t tile = static_cast<uint32_t>(min(n_blk / kTileN + wn * WN + j, a.n_tiles - 1));
     code_off[j] = tile * ng * kUnitBytes;
     scale_off[j] = static_cast<uint32_t>(a.scales_off) + tile * ng * (2 * kTileN);
-    zero_off[j] = asym ? static_cast<uint32_t>(a.zeros_off) + tile * ng * 8 : 0u;
+    zero_off[j] = ASYM ? static_cast<uint32_t>(a.zeros_off) + tile * ng * 8 : 0u;
   }
   const uint32_t lane_code = 16u * lane, lane_scale = 2u * r, lane_zero = 4u * (r >> 3);
   const int zshift = 4 * (r & 7);
 
-  // X' rows of this block as one buffer resource (rows past M read as 0)
+  // X' rows of this block as one buffer resource (rows past M read as 0), and inv_s_c
+  // (an empty resource when the activations come pre-scaled)
   const int rows_here = min(BM, a.M - m_blk);
   const __amdgpu_buffer_rsrc_t rx =
       make_rsrc(a.x + static_cast<int64_t>(m_blk) * a.K, static_cast<uint32_t>(rows_here) * a.K * 2);
+  const __amdgpu_buffer_rsrc_t rinv =
+      make_rsrc(has_inv ? a.inv : a.x, has_inv ? static_cast<uint32_t>(a.K) * 2 : 0u);
+  // thread -> X' vectors: rows tid / 16 + 16 it, channels 8 (tid % 16)..+7 of the group
+  const int a_col = (threadIdx.x & 15) * 8;
   uint32_t a_voff[A_VEC];
-  int a_lds[A_VEC], a_col[A_VEC];
+  int a_lds[A_VEC];
 #pragma unroll
   for (int it = 0; it < A_VEC; ++it) {
-    const int v = threadIdx.x + it * kGThreads;
-    const int row = v >> 4, col = (v & 15) * 8;
-    a_voff[it] = static_cast<uint32_t>(row * a.K + col) * 2;
-    a_lds[it] = row * kLdsStride + col;
-    a_col[it] = col;
+    const int row = (threadIdx.x + it * kGThreads) >> 4;
+    a_voff[it] = static_cast<uint32_t>(row * a.K + a_col) * 2;
+    a_lds[it] = row * kLdsStride + a_col;
   }
 
+  // Every load below is issued unconditionally; a group past the last one gets a lane
+  // offset past the end of its resource and reads zeros without touching memory. With
+  // no branches around loads, each wait covers exactly the loads it needs.
   uint4 areg[A_VEC];
+  uint4 ireg;
   auto load_a = [&](int g) {
+    const bool live = g < ng;
+    const uint32_t skip = live ? 0u : kNoLoad;
+    const uint32_t soff = live ? static_cast<uint32_t>(g) * kGroup * 2 : 0u;
 #pragma unroll
-    for (int it = 0; it < A_VEC; ++it) areg[it] = buf_load16(rx, a_voff[it], g * kGroup * 2);
+    for (int it = 0; it < A_VEC; ++it) areg[it] = buf_load16(rx, a_voff[it] + skip, soff);
+    ireg = buf_load16(rinv, 2u * a_col + skip, soff);
   };
-  auto store_a = [&](int g, int buf) {
+  // X' = binary16(x * inv); with no inv_s_c the factor is 1 (exact). A select rather
+  // than a branch keeps the inv_s_c load unconditional.
+  const uint4 ones = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+  auto store_a = [&](int buf) {
     _Float16* dst = xs + buf * BUF;
-    if (a.inv) {
+    const uint4 iv = has_inv ? ireg : ones;
 #pragma unroll
-      for (int it = 0; it < A_VEC; ++it) {
-        const uint4 iv = *reinterpret_cast<const uint4*>(a.inv + g * kGroup + a_col[it]);
-        *reinterpret_cast<uint4*>(dst + a_lds[it]) = scale_x(areg[it], iv);
-      }
-    } else {
-#pragma unroll
-      for (int it = 0; it < A_VEC; ++it) *reinterpret_cast<uint4*>(dst + a_lds[it]) = areg[it];
-    }
+    for (int it = 0; it < A_VEC; ++it) *reinterpret_cast<uint4*>(dst + a_lds[it]) = scale_x(areg[it], iv);
   };
   struct BRegs {
     uint4 c[WN];
     uint32_t s[WN], z[WN];
   };
   auto load_b = [&](BRegs& b, int g) {
+    const bool live = g < ng;
+    const uint32_t skip = live ? 0u : kNoLoad;
+    const uint32_t gg = live ? static_cast<uint32_t>(g) : 0u;
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
-      b.c[j] = buf_load16(rp, lane_code, code_off[j] + g * kUnitBytes);
-      b.s[j] = buf_load2(rp, lane_scale, scale_off[j] + g * (2 * kTileN));
-      b.z[j] = asym ? buf_load4(rp, lane_zero, zero_off[j] + g * 8) : 0u;
+      b.c[j] = buf_load16(rp, lane_code + skip, code_off[j] + gg * kUnitBytes);
+      b.s[j] = buf_load2(rp, lane_scale + skip, scale_off[j] + gg * (2 * kTileN));
+      if (ASYM) b.z[j] = buf_load4(rp, lane_zero + skip, zero_off[j] + gg * 8);
     }
   };
 
@@ -153,7 +166,7 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
     uint32_t nz1024[WN], nz64[WN];
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
-      const uint32_t z = asym ? (b.z[j] >> zshift) & 0xFu : 8u;
+      const uint32_t z = ASYM ? (b.z[j] >> zshift) & 0xFu : 8u;
       s2[j] = as_h2(b.s[j] | (b.s[j] << 16));
       nz1024[j] = neg_off1024(z);
       nz64[j] = neg_off64(z);
@@ -192,28 +205,30 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
   BRegs b0, b1;
   load_a(0);
   load_b(b0, 0);
-  store_a(0, 0);
-  if (ng > 1) load_a(1);
+  store_a(0);
+  load_a(1);
   __syncthreads();
 
-  int g = 0;
-  for (; g + 1 < ng; g += 2) {
-    // even group: compute from buffer 0 with b0; prefetch B(g+1); stage X'(g+1)
+  // two groups per trip: g from buffer 0 / b0, g + 1 from buffer 1 / b1. While one group
+  // is multiplied, the weights of the next are in flight and its X' goes into the other
+  // LDS buffer; one barrier per group.
+  // (sched_barrier keeps the scheduler from sinking the prefetches below the math)
+  for (int g = 0; g < ng; g += 2) {
     load_b(b1, g + 1);
+    __builtin_amdgcn_sched_barrier(0);
     compute(b0, 0);
-    store_a(g + 1, 1);
-    if (g + 2 < ng) load_a(g + 2);
+    store_a(1);
+    load_a(g + 2);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    // odd group: compute from buffer 1 with b1
-    if (g + 2 < ng) load_b(b0, g + 2);
-    compute(b1, 1);
-    if (g + 2 < ng) {
-      store_a(g + 2, 0);
-      if (g + 3 < ng) load_a(g + 3);
-    }
+    load_b(b0, g + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (g + 1 < ng) compute(b1, 1);
+    store_a(0);
+    load_a(g + 3);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   }
-  if (g < ng) compute(b0, 0);  // odd number of groups: the last one is in buffer 0
 
   // epilogue: element q of acc[ms][j] is row 4 (l / 16) + q, column l % 16 of its tile
 #pragma unroll
@@ -233,13 +248,13 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
   }
 }
 
-template <int WAVES_M, int WM, int WN, int SCHED = 0>
-hipError_t launch_tiles(GemmArgs a, hipStream_t st) {
+template <int WAVES_M, int WM, int WN, int SCHED, bool ASYM>
+hipError_t launch_tiles_fmt(GemmArgs a, hipStream_t st) {
   constexpr int BM = WAVES_M * WM * 16, BN = (4 / WAVES_M) * WN * 16;
   const size_t lds = 2ull * BM * kLdsStride * sizeof(_Float16);
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<WAVES_M, WM, WN, SCHED>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<WAVES_M, WM, WN, SCHED, ASYM>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
@@ -248,8 +263,14 @@ hipError_t launch_tiles(GemmArgs a, hipStream_t st) {
   a.n_blocks_m = (a.M + BM - 1) / BM;
   a.n_blocks_n = (a.N + BN - 1) / BN;
   const unsigned blocks = static_cast<unsigned>(a.n_blocks_m) * static_cast<unsigned>(a.n_blocks_n);
-  hipLaunchKernelGGL((gemm_kernel<WAVES_M, WM, WN, SCHED>), dim3(blocks), dim3(kGThreads), lds, st, a);
+  hipLaunchKernelGGL((gemm_kernel<WAVES_M, WM, WN, SCHED, ASYM>), dim3(blocks), dim3(kGThreads), lds, st, a);
   return hipGetLastError();
+}
+
+template <int WAVES_M, int WM, int WN, int SCHED = 0>
+hipError_t launch_tiles(GemmArgs a, hipStream_t st) {
+  if (a.zeros_off >= 0) return launch_tiles_fmt<WAVES_M, WM, WN, SCHED, true>(a, st);
+  return launch_tiles_fmt<WAVES_M, WM, WN, SCHED, false>(a, st);
 }
 
 }  // namespace
@@ -297,8 +318,10 @@ hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* p
   }
   // Defaults from sweeps on MI355X: at M <= 64 the product is bound by streaming the
   // weights, and narrow 64 x 128 workgroup tiles give the most workgroups; at larger M a
-  // 64 x 256 tile (each wavefront 64 x 64) runs best.
+  // 64 x 256 tile (each wavefront 64 x 64) runs best, or for long K or wide N a 128 x 128
+  // tile (each wavefront 128 x 32), which dequantizes each weight fragment for 8 row tiles.
   if (M <= 64) return launch_tiles<1, 4, 2>(a, st);
+  if (K >= 8192 || N >= 16384) return launch_tiles<1, 8, 2>(a, st);
   return launch_tiles<1, 4, 4>(a, st);
 }
 

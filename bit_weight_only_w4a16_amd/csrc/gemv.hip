@@ -10,6 +10,12 @@
 //  * its wavefronts take interleaved 128-channel groups; for each group one wavefront
 //    load moves a whole 1 KiB unit (one 128-bit load per lane, fully coalesced), and the
 //    loads of the next batch of groups are issued before the current batch is consumed;
+//  * every load is issued unconditionally: a load with nothing to fetch gets a per-lane
+//    offset past the end of its buffer resource, which returns zeros without a memory
+//    access. With no branch around a load the compiler's wait counts are exact, so a
+//    wavefront waits for the batch it is about to use and never for the one behind it;
+//  * the activations are requested before the weights, so staging them waits only for
+//    the activation loads;
 //  * dequantization is folded into the dot products: a nibble OR-ed into binary16 1024
 //    (or 64) is (off + q) exactly, v_dot2_f32_f16 accumulates X' * (off + q) in float32,
 //    and per group y += s * (acc - O - z * S), where O = sum X' * off and S = sum X' over
@@ -35,62 +41,81 @@ struct GemvArgs {
   const uint8_t* packed;
   uint16_t* y;
   int64_t scales_off;
-  int64_t zeros_off;  // < 0: symmetric format (zero 8)
+  int64_t zeros_off;
   int N, K, n_groups, phase_groups;
 };
 
-// X' for channels [k0, k0 + nk) of every row into xs[m][nk], and O, S for every
-// 32-channel slice into osum/ssum[m][nk / 32]. A thread converts 8 channels; the 4
-// threads of a slice are consecutive lanes and add their partial sums with shuffles.
-// Channel k of a word has offset 1024 if k % 8 is in {0, 1, 4, 5}, else 64.
-template <int M, int NT>
-__device__ __forceinline__ void stage_phase(const GemvArgs& a, int k0, int nk, _Float16* xs,
-                                            float* osum, float* ssum) {
-  const int vec_per_row = nk / 8;  // a multiple of 16
+// Staging of X' for channels [k0, k0 + nk) of every row: thread `tid` handles the 8-channel
+// vectors i = tid + NT * j (row i / (nk / 8)). Loads come from buffer resources, so a
+// vector past the end reads zeros and no load needs a branch.
+struct XStage {
+  __amdgpu_buffer_rsrc_t rx, rinv;
+  int vpr;    // vectors per row in this phase (a multiple of 16)
+  int total;  // M * vpr
+  int k0;
+};
+
+__device__ __forceinline__ uint32_t x_voff(const GemvArgs& a, const XStage& s, int i) {
+  const int m = i / s.vpr, v = i - m * s.vpr;
+  const uint32_t off = 2u * static_cast<uint32_t>(m * a.K + s.k0 + 8 * v);
+  return i < s.total ? off : kNoLoad;
+}
+__device__ __forceinline__ uint32_t inv_voff(const XStage& s, int i) {
+  const int v = i % s.vpr;
+  return i < s.total ? 2u * static_cast<uint32_t>(s.k0 + 8 * v) : kNoLoad;
+}
+
+// X' = binary16(x * inv) for one vector; writes it and, from the first lane of each
+// group of 4 (one 32-channel slice), O and S for the slice. Channel k of a word has
+// offset 1024 if k % 8 is in {0, 1, 4, 5}, else 64. All four lanes of a slice are
+// active together: `total` is a multiple of 16 and NT of 64.
+__device__ __forceinline__ void stage_store(const XStage& s, int i, uint4 val, uint4 iv,
+                                            bool has_inv, int nk, _Float16* xs, float* osum,
+                                            float* ssum) {
   const half2_t one2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
   const half2_t o1024 = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
   const half2_t o64 = {static_cast<_Float16>(64.0f), static_cast<_Float16>(64.0f)};
-  for (int i = threadIdx.x; i < M * vec_per_row; i += NT) {
-    const int m = i / vec_per_row, v = i - m * vec_per_row;
-    uint4 val = *reinterpret_cast<const uint4*>(a.x + static_cast<int64_t>(m) * a.K + k0 + 8 * v);
-    if (a.inv) {
-      const uint4 iv = *reinterpret_cast<const uint4*>(a.inv + k0 + 8 * v);
-      const uint32_t xw[4] = {val.x, val.y, val.z, val.w};
-      const uint32_t iw[4] = {iv.x, iv.y, iv.z, iv.w};
-      uint32_t ow[4];
+  // with no inv_s_c the factor is 1 (exact); a select rather than a branch keeps the
+  // inv_s_c load unconditional
+  if (!has_inv) iv = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+  {
+    const uint32_t xw[4] = {val.x, val.y, val.z, val.w};
+    const uint32_t iw[4] = {iv.x, iv.y, iv.z, iv.w};
+    uint32_t ow[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const half2_t xh = as_h2(xw[j]), ih = as_h2(iw[j]);
-        half2_t rr;
-        rr.x = static_cast<_Float16>(static_cast<float>(xh.x) * static_cast<float>(ih.x));
-        rr.y = static_cast<_Float16>(static_cast<float>(xh.y) * static_cast<float>(ih.y));
-        ow[j] = as_u32(rr);
-      }
-      val = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+    for (int j = 0; j < 4; ++j) {
+      const half2_t xh = as_h2(xw[j]), ih = as_h2(iw[j]);
+      half2_t rr;
+      rr.x = static_cast<_Float16>(static_cast<float>(xh.x) * static_cast<float>(ih.x));
+      rr.y = static_cast<_Float16>(static_cast<float>(xh.y) * static_cast<float>(ih.y));
+      ow[j] = as_u32(rr);
     }
+    val = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+  }
+  float sv = __builtin_amdgcn_fdot2(as_h2(val.x), one2, 0.0f, false);
+  sv = __builtin_amdgcn_fdot2(as_h2(val.y), one2, sv, false);
+  sv = __builtin_amdgcn_fdot2(as_h2(val.z), one2, sv, false);
+  sv = __builtin_amdgcn_fdot2(as_h2(val.w), one2, sv, false);
+  float ov = __builtin_amdgcn_fdot2(as_h2(val.x), o1024, 0.0f, false);
+  ov = __builtin_amdgcn_fdot2(as_h2(val.y), o64, ov, false);
+  ov = __builtin_amdgcn_fdot2(as_h2(val.z), o1024, ov, false);
+  ov = __builtin_amdgcn_fdot2(as_h2(val.w), o64, ov, false);
+  sv += __shfl_xor(sv, 1, 4);
+  ov += __shfl_xor(ov, 1, 4);
+  sv += __shfl_xor(sv, 2, 4);
+  ov += __shfl_xor(ov, 2, 4);
+  if (i < s.total) {
+    const int m = i / s.vpr, v = i - m * s.vpr;
     *reinterpret_cast<uint4*>(xs + m * nk + 8 * v) = val;
-    float sv = __builtin_amdgcn_fdot2(as_h2(val.x), one2, 0.0f, false);
-    sv = __builtin_amdgcn_fdot2(as_h2(val.y), one2, sv, false);
-    sv = __builtin_amdgcn_fdot2(as_h2(val.z), one2, sv, false);
-    sv = __builtin_amdgcn_fdot2(as_h2(val.w), one2, sv, false);
-    float ov = __builtin_amdgcn_fdot2(as_h2(val.x), o1024, 0.0f, false);
-    ov = __builtin_amdgcn_fdot2(as_h2(val.y), o64, ov, false);
-    ov = __builtin_amdgcn_fdot2(as_h2(val.z), o1024, ov, false);
-    ov = __builtin_amdgcn_fdot2(as_h2(val.w), o64, ov, false);
-    sv += __shfl_xor(sv, 1, 4);
-    ov += __shfl_xor(ov, 1, 4);
-    sv += __shfl_xor(sv, 2, 4);
-    ov += __shfl_xor(ov, 2, 4);
     if ((v & 3) == 0) {
       const int e = m * (nk / 32) + (v >> 2);
       ssum[e] = sv;
       osum[e] = ov;
     }
   }
-  __syncthreads();
 }
 
-template <int M, int WAVES, int BATCH>
+template <int M, int WAVES, int BATCH, bool ASYM>
 __global__ void __launch_bounds__(WAVES * 64) gemv_kernel(GemvArgs a) {
   constexpr int NT = WAVES * 64;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -100,6 +125,7 @@ __global__ void __launch_bounds__(WAVES * 64) gemv_kernel(GemvArgs a) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, p = lane >> 4;
   const int ng = a.n_groups;
+  const bool has_inv = a.inv != nullptr;
 
   _Float16* xs = reinterpret_cast<_Float16*>(smem);
   float* osum = reinterpret_cast<float*>(smem + 2 * M * a.phase_groups * kGroup);
@@ -112,11 +138,14 @@ __global__ void __launch_bounds__(WAVES * 64) gemv_kernel(GemvArgs a) {
       make_rsrc(a.packed + static_cast<int64_t>(t) * ng * kUnitBytes, ng * kUnitBytes);
   const __amdgpu_buffer_rsrc_t rscales =
       make_rsrc(a.packed + a.scales_off + static_cast<int64_t>(t) * ng * (2 * kTileN), ng * 2 * kTileN);
-  const bool asym = a.zeros_off >= 0;
   const __amdgpu_buffer_rsrc_t rzeros =
-      make_rsrc(a.packed + (asym ? a.zeros_off : 0) + static_cast<int64_t>(t) * ng * 8, ng * 8);
+      make_rsrc(a.packed + (ASYM ? a.zeros_off : 0) + static_cast<int64_t>(t) * ng * 8, ng * 8);
   const uint32_t lane_code = 16u * lane, lane_scale = 2u * r, lane_zero = 4u * (r >> 3);
   const int zshift = 4 * (r & 7);
+
+  XStage xst;
+  xst.rx = make_rsrc(a.x, static_cast<uint32_t>(M * a.K * 2));
+  xst.rinv = make_rsrc(has_inv ? a.inv : a.x, has_inv ? static_cast<uint32_t>(a.K * 2) : 0u);
 
   float yacc[M];
 #pragma unroll
@@ -126,15 +155,16 @@ __global__ void __launch_bounds__(WAVES * 64) gemv_kernel(GemvArgs a) {
     uint4 c[BATCH];
     uint32_t s[BATCH], z[BATCH];
   };
+  // groups gl = wave + WAVES * j of the phase, j < nj; a slot past nj loads nothing
   auto load = [&](Batch& b, int ph0, int jb, int nj) {
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
-      if (jb + u < nj) {
-        const uint32_t g = static_cast<uint32_t>(ph0 + wave + WAVES * (jb + u));
-        b.c[u] = buf_load16(rcodes, lane_code, g * kUnitBytes);
-        b.s[u] = buf_load2(rscales, lane_scale, g * (2 * kTileN));
-        b.z[u] = asym ? buf_load4(rzeros, lane_zero, g * 8) : 0u;
-      }
+      const bool live = jb + u < nj;
+      const uint32_t g = live ? static_cast<uint32_t>(ph0 + wave + WAVES * (jb + u)) : 0u;
+      const uint32_t skip = live ? 0u : kNoLoad;
+      b.c[u] = buf_load16(rcodes, lane_code + skip, g * kUnitBytes);
+      b.s[u] = buf_load2(rscales, lane_scale + skip, g * (2 * kTileN));
+      if (ASYM) b.z[u] = buf_load4(rzeros, lane_zero + skip, g * 8);
     }
   };
   auto compute = [&](const Batch& b, int jb, int nj, int ngp, int nk) {
@@ -160,7 +190,7 @@ __global__ void __launch_bounds__(WAVES * 64) gemv_kernel(GemvArgs a) {
           }
         }
         const float s = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b.s[u])));
-        const float z = asym ? static_cast<float>((b.z[u] >> zshift) & 0xFu) : 8.0f;
+        const float z = ASYM ? static_cast<float>((b.z[u] >> zshift) & 0xFu) : 8.0f;
 #pragma unroll
         for (int m = 0; m < M; ++m) {
           const int e = (m * ngp + gl) * 4 + p;
@@ -173,12 +203,27 @@ __global__ void __launch_bounds__(WAVES * 64) gemv_kernel(GemvArgs a) {
   for (int ph0 = 0; ph0 < ng; ph0 += a.phase_groups) {
     const int ngp = min(a.phase_groups, ng - ph0);
     const int nk = ngp * kGroup;
-    // this wavefront's groups in the phase: gl = wave + WAVES * j, j < nj
+    xst.vpr = nk / 8;
+    xst.total = M * xst.vpr;
+    xst.k0 = ph0 * kGroup;
+    // activations first (two vectors per thread), then this wavefront's first batch
+    const int i0 = threadIdx.x, i1 = threadIdx.x + NT;
+    const uint4 x0 = buf_load16(xst.rx, x_voff(a, xst, i0), 0);
+    const uint4 v0 = buf_load16(xst.rinv, inv_voff(xst, i0), 0);
+    const uint4 x1 = buf_load16(xst.rx, x_voff(a, xst, i1), 0);
+    const uint4 v1 = buf_load16(xst.rinv, inv_voff(xst, i1), 0);
     const int nj = wave < ngp ? (ngp - wave + WAVES - 1) / WAVES : 0;
     Batch b0, b1;
     load(b0, ph0, 0, nj);
     if (ph0 != 0) __syncthreads();  // the previous phase is done with LDS
-    stage_phase<M, NT>(a, ph0 * kGroup, nk, xs, osum, ssum);
+    stage_store(xst, i0, x0, v0, has_inv, nk, xs, osum, ssum);
+    stage_store(xst, i1, x1, v1, has_inv, nk, xs, osum, ssum);
+    for (int i = threadIdx.x + 2 * NT; i < ((xst.total + NT - 1) / NT) * NT; i += NT) {
+      const uint4 xv = buf_load16(xst.rx, x_voff(a, xst, i), 0);
+      const uint4 iv = buf_load16(xst.rinv, inv_voff(xst, i), 0);
+      stage_store(xst, i, xv, iv, has_inv, nk, xs, osum, ssum);
+    }
+    __syncthreads();
     for (int jb = 0; jb < nj; jb += 2 * BATCH) {
       load(b1, ph0, jb + BATCH, nj);
       compute(b0, jb, nj, ngp, nk);
@@ -208,12 +253,6 @@ __global__ void __launch_bounds__(WAVES * 64) gemv_kernel(GemvArgs a) {
   }
 }
 
-// Two groups in flight per wavefront per batch (double-buffered), and 16 wavefronts per
-// workgroup when there are few tiles (N <= 8192: one workgroup per CU, more loads in
-// flight per CU), 8 otherwise (several workgroups per CU).
-constexpr int kBatchDefault = 2;
-inline bool many_waves(int64_t n_tiles) { return n_tiles <= 512; }
-
 int phase_groups_for(int M, int n_groups) {
   int pg = kLdsBudget / (M * (2 * kGroup + 32));
   if (pg > n_groups) pg = n_groups;
@@ -228,15 +267,23 @@ size_t smem_bytes(int M, int phase_groups, int waves) {
 template <int M, int WAVES, int BATCH>
 hipError_t launch_cfg(const GemvArgs& a, int64_t n_tiles, hipStream_t st) {
   const size_t lds = smem_bytes(M, a.phase_groups, WAVES);
-  hipLaunchKernelGGL((gemv_kernel<M, WAVES, BATCH>), dim3(static_cast<unsigned>(n_tiles)),
-                     dim3(WAVES * 64), lds, st, a);
+  if (a.zeros_off >= 0) {
+    hipLaunchKernelGGL((gemv_kernel<M, WAVES, BATCH, true>), dim3(static_cast<unsigned>(n_tiles)),
+                       dim3(WAVES * 64), lds, st, a);
+  } else {
+    hipLaunchKernelGGL((gemv_kernel<M, WAVES, BATCH, false>), dim3(static_cast<unsigned>(n_tiles)),
+                       dim3(WAVES * 64), lds, st, a);
+  }
   return hipGetLastError();
 }
 
+// Eight wavefronts with two groups in flight each; for long rows (K >= 16384) sixteen
+// wavefronts with one group each, which keeps more loads in flight per CU when there are
+// few tiles per CU. (Sweeps on MI355X over 4096 <= K, N <= 28672.)
 template <int M>
 hipError_t launch_m(const GemvArgs& a, int64_t n_tiles, hipStream_t st) {
-  if (many_waves(n_tiles)) return launch_cfg<M, 16, kBatchDefault>(a, n_tiles, st);
-  return launch_cfg<M, 8, kBatchDefault>(a, n_tiles, st);
+  if (a.n_groups >= 128) return launch_cfg<M, 16, 1>(a, n_tiles, st);
+  return launch_cfg<M, 8, 2>(a, n_tiles, st);
 }
 
 // Tuning override for sweeps (M = 1 only): AWQ_GEMV_CFG = "waves,batch".
@@ -245,7 +292,6 @@ hipError_t launch_m1(const GemvArgs& a, int64_t n_tiles, hipStream_t st) {
   if (env) {
     int w = 0, b = 0;
     if (sscanf(env, "%d,%d", &w, &b) == 2) {
-      if (w == 4 && b == 4) return launch_cfg<1, 4, 4>(a, n_tiles, st);
       if (w == 8 && b == 1) return launch_cfg<1, 8, 1>(a, n_tiles, st);
       if (w == 8 && b == 2) return launch_cfg<1, 8, 2>(a, n_tiles, st);
       if (w == 8 && b == 4) return launch_cfg<1, 8, 4>(a, n_tiles, st);

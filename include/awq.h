@@ -26,7 +26,7 @@
  *       X [M][K], y [M][N] binary16
  *   - Formats: AWQ_FMT_ASYM (scale + zero point), AWQ_FMT_SYM8 (zero fixed at 8).
  *   - Shapes: N % 8 == 0, K % group == 0, group == 128 (the only group size the
- *     kernels are built for; others return AWQ_ERR_UNSUPPORTED), N*K < 2^32,
+ *     kernels are built for; others return AWQ_ERR_UNSUPPORTED), N*K < 2^31,
  *     K <= 2^22, M*K < 2^32 and M*N < 2^32 (AWQ_ERR_UNSUPPORTED beyond).
  *   - Pointers marked "device" must be device (HBM) addresses on the current HIP
  *     device, 16-byte aligned (AWQ_ERR_MISALIGNED otherwise). The library never

@@ -94,6 +94,16 @@ def test_gemm_validation(lib):
     assert lib.awq_gemm(P, None, P + 4, 9, 64, 128, 128, 0, P, None, 0, None) == MISALIGNED
 
 
+def test_layer_size_limit(lib):
+    # N * K must stay below 2^31 (offsets into one layer fit in 31 bits)
+    k = 1 << 16
+    n_ok, n_big = (1 << 15) - 8, 1 << 15
+    assert lib.awq_repacked_bytes(n_ok, k, 128, 0) > 0
+    assert lib.awq_repacked_bytes(n_big, k, 128, 0) == 0
+    assert lib.awq_gemv(P, None, P, 1, n_big, k, 128, 0, P, None, 0, None) == UNSUPPORTED
+    assert lib.awq_gemm(P, None, P, 16, n_big, k, 128, 0, P, None, 0, None) == UNSUPPORTED
+
+
 def test_pack_and_repack_validation(lib):
     # qzeros must be given for the asymmetric format and NULL for the symmetric one
     assert lib.awq_pack(P, None, 64, 128, 128, 0, P, P, None, None) == INVALID
