@@ -185,7 +185,7 @@ def _product(fn_name, x, inv_s_c, packed, n, k, group, fmt, y, ws):
 
 def awq_gemv(x, inv_s_c, packed, n: int, k: int, group: int = GROUP, fmt: int = FMT_ASYM,
              y=None, ws=None) -> torch.Tensor:
-    """Decode product, 1 <= M <= 8."""
+    """Decode product, 1 <= M <= 16."""
     return _product("awq_gemv", x, inv_s_c, packed, n, k, group, fmt, y, ws)
 
 

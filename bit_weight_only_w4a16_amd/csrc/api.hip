@@ -125,7 +125,7 @@ int awq_dequant(const void* w, const uint16_t* scales, const int32_t* qzeros, in
 
 size_t awq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group) {
   if (M <= 0 || check_shape(N, K, group, AWQ_FMT_ASYM) != AWQ_OK) return 0;
-  const size_t a = M <= 8 ? awq::gemv_workspace_bytes(M, N, K) : 0;
+  const size_t a = M <= 16 ? awq::gemv_workspace_bytes(M, N, K) : 0;
   const size_t b = awq::gemm_workspace_bytes(M, N, K);
   return a > b ? a : b;
 }
@@ -135,7 +135,7 @@ int awq_gemv(const uint16_t* x, const uint16_t* inv_s_c, const void* packed, int
              size_t ws_bytes, hipStream_t stream) {
   int rc = check_product(x, inv_s_c, packed, M, N, K, group, fmt, y, ws, ws_bytes);
   if (rc != AWQ_OK) return rc;
-  if (M > 8) return AWQ_ERR_UNSUPPORTED;
+  if (M > 16) return AWQ_ERR_UNSUPPORTED;
   if (M == 0) return AWQ_OK;
   return hip_status(awq::launch_gemv(x, inv_s_c, packed, M, N, K, fmt, y, ws, ws_bytes, stream));
 }

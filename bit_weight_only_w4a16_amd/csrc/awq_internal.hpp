@@ -185,6 +185,15 @@ __device__ __forceinline__ uint32_t as_u32(half2_t h) {
 
 // Exact dequantization of one word: eight binary16 values (q - z) * s in channel order.
 // (off + q) - (off + z) is an exact small integer; one binary16 multiply rounds once.
+// binary16(x * inv) for 8 channels (v_pk_mul_f16): the product of two binary16 values
+// is exact before its one rounding to nearest even, as in the definition X' = X * inv_s_c
+// rounded to binary16.
+__device__ __forceinline__ uint4 scale_x8(uint4 val, uint4 iv) {
+  const half2_t a0 = as_h2(val.x) * as_h2(iv.x), a1 = as_h2(val.y) * as_h2(iv.y);
+  const half2_t a2 = as_h2(val.z) * as_h2(iv.z), a3 = as_h2(val.w) * as_h2(iv.w);
+  return make_uint4(as_u32(a0), as_u32(a1), as_u32(a2), as_u32(a3));
+}
+
 __device__ __forceinline__ void dequant_word(uint32_t w, uint32_t nz1024, uint32_t nz64,
                                              half2_t s2, half2_t out[4]) {
   const Pairs4 pr = unpack_word(w);

@@ -50,13 +50,6 @@ struct GemmArgs {
   int M, N, K, n_groups, n_tiles, n_blocks_n, n_blocks_m;
 };
 
-__device__ __forceinline__ uint4 scale_x(uint4 val, uint4 iv) {
-  // binary16(x * inv): the product of two binary16 values is exact before the rounding
-  const half2_t a0 = as_h2(val.x) * as_h2(iv.x), a1 = as_h2(val.y) * as_h2(iv.y);
-  const half2_t a2 = as_h2(val.z) * as_h2(iv.z), a3 = as_h2(val.w) * as_h2(iv.w);
-  return make_uint4(as_u32(a0), as_u32(a1), as_u32(a2), as_u32(a3));
-}
-
 // SCHED > 0: ask the scheduler to issue each matrix instruction followed by SCHED VALU
 // instructions (and an LDS read every WN of them), so that the dequantization of the
 // next weight fragments runs while the matrix core is busy.
@@ -136,7 +129,7 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
     _Float16* dst = xs + buf * BUF;
     const uint4 iv = has_inv ? ireg : ones;
 #pragma unroll
-    for (int it = 0; it < A_VEC; ++it) *reinterpret_cast<uint4*>(dst + a_lds[it]) = scale_x(areg[it], iv);
+    for (int it = 0; it < A_VEC; ++it) *reinterpret_cast<uint4*>(dst + a_lds[it]) = scale_x8(areg[it], iv);
   };
   struct BRegs {
     uint4 c[WN];

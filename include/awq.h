@@ -160,7 +160,7 @@ int awq_dequant(const void* w, const uint16_t* scales, const int32_t* qzeros,
 size_t awq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group);
 
 /*
- * awq_gemv - decode product for 1 <= M <= 8 activation rows (edgesiliconlab ?p=2015,
+ * awq_gemv - decode product for 1 <= M <= 16 activation rows (edgesiliconlab ?p=2015,
  * sections "The Mathematics of Memory Bandwidth Saturation" and "GEMM vs. GEMV
  * Kernels and Batch Size Dynamics": at batch 1 the product streams every weight once
  * and is bound by memory bandwidth).
@@ -175,7 +175,7 @@ size_t awq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group);
  *         ws_bytes == 0.
  * M == 0 returns AWQ_OK without launching. Deterministic: the same inputs give the
  * same bits on every call.
- * Errors: INVALID_ARG, UNSUPPORTED (M > 8, group), MISALIGNED, WORKSPACE, HIP.
+ * Errors: INVALID_ARG, UNSUPPORTED (M > 16, group), MISALIGNED, WORKSPACE, HIP.
  */
 int awq_gemv(const uint16_t* x, const uint16_t* inv_s_c, const void* packed, int64_t M,
              int64_t N, int64_t K, int32_t group, int32_t fmt, uint16_t* y, void* ws,

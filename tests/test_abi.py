@@ -80,7 +80,7 @@ P = 4096  # an aligned stand-in address; never dereferenced because validation f
     ((P + 2, None, P, 1, 64, 128, 128, 0, P, None, 0, None), MISALIGNED),  # x
     ((P, P + 8, P, 1, 64, 128, 128, 0, P, None, 0, None), MISALIGNED),     # inv_s_c
     ((P, None, P, 1, 64, 128, 128, 0, P, None, 16, None), INVALID),        # ws NULL, bytes
-    ((P, None, P, 9, 64, 128, 128, 0, P, None, 0, None), UNSUPPORTED),     # M > 8 (gemv)
+    ((P, None, P, 17, 64, 128, 128, 0, P, None, 0, None), UNSUPPORTED),    # M > 16 (gemv)
     ((None, None, None, 0, 64, 128, 128, 0, None, None, 0, None), OK),     # M == 0: no-op
 ])
 def test_gemv_validation(lib, args, code):

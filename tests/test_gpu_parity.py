@@ -217,7 +217,7 @@ def product_case(n, k, m, fmt, seed=0):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
-@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 13, 16])
 @pytest.mark.parametrize("n,k", [(512, 512), (200, 1024), (72, 256), (1000, 3072)])
 def test_gemv_parity(n, k, m, fmt):
     d, g, o, y_ref = product_case(n, k, m, fmt)
@@ -225,7 +225,7 @@ def test_gemv_parity(n, k, m, fmt):
     ws = awq.workspace(m, n, k, DEV)
     y = awq.awq_gemv(x, g["inv"], g["packed"], n, k, 128, fmt, ws=ws)
     assert rel_err(y.cpu().numpy(), y_ref) <= TOL
-    y2 = awq.awq_gemv(x, g["inv"], g["packed"], n, k, 128, fmt, ws=None)   # no split-K
+    y2 = awq.awq_gemv(x, g["inv"], g["packed"], n, k, 128, fmt, ws=None)   # no workspace
     assert rel_err(y2.cpu().numpy(), y_ref) <= TOL
 
 
@@ -289,6 +289,7 @@ FULL = [
     ("7b_gateup_m1", 11008, 4096, 1, 0, "gemv"),
     ("7b_down_m1", 4096, 11008, 1, 0, "gemv"),
     ("batched_m8", 11008, 4096, 8, 0, "gemv"),
+    ("batched_m16_gemv", 11008, 4096, 16, 0, "gemv"),
     ("batched_m16", 11008, 4096, 16, 0, "gemm"),
     ("batched_m64", 11008, 4096, 64, 0, "gemm"),
     ("prefill_qkv_m2048", 6144, 4096, 2048, 0, "gemm"),
