@@ -201,8 +201,8 @@ _WS = {}
 
 
 def workspace(m: int, n: int, k: int, device, group: int = GROUP) -> torch.Tensor | None:
-    """A zero-filled workspace large enough for (m, n, k), cached per device and grown
-    on demand (the library returns its counters to zero after every call)."""
+    """A workspace large enough for (m, n, k), cached per device and grown on demand
+    (the library overwrites what it uses on every call; no initialisation needed)."""
     need = awq_workspace_bytes(m, n, k, group)
     if need == 0:
         return None
@@ -210,7 +210,7 @@ def workspace(m: int, n: int, k: int, device, group: int = GROUP) -> torch.Tenso
     key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
     cur = _WS.get(key)
     if cur is None or cur.numel() < need:
-        cur = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=dev)
+        cur = torch.empty(max(need, 1 << 20), dtype=torch.uint8, device=dev)
         _WS[key] = cur
     return cur
 

@@ -44,7 +44,6 @@ def hipcc() -> str:
 # register allocator copies accumulators between AGPRs inside the main loop.
 FILE_FLAGS = {
     "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-    "gemm_lds.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 

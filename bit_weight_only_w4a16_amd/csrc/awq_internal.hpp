@@ -61,9 +61,6 @@ hipError_t launch_gemv(const uint16_t* x, const uint16_t* inv_s_c, const void* p
                        int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y, void* ws,
                        size_t ws_bytes, hipStream_t st);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
-hipError_t launch_gemm_lds(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
-                           int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y, int cfg,
-                           hipStream_t st);
 hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
                        int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y, void* ws,
                        size_t ws_bytes, hipStream_t st);

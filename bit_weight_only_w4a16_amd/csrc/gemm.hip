@@ -47,7 +47,8 @@ struct GemmArgs {
   int64_t scales_off;
   int64_t zeros_off;
   uint32_t packed_bytes;
-  int M, N, K, n_groups, n_tiles, n_blocks_n, n_blocks_m;
+  float* part;  // split-K partial sums [splits][M][N], or NULL (one split)
+  int M, N, K, n_groups, n_tiles, n_blocks_n, n_blocks_m, splits;
 };
 
 // SCHED > 0: ask the scheduler to issue each matrix instruction followed by SCHED VALU
@@ -75,6 +76,9 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
   const int m_blk = bm * BM, n_blk = bn * BN;
   const int ng = a.n_groups;
   const bool has_inv = a.inv != nullptr;
+  // this workgroup's share of K: groups [g0, g1)
+  const int split = blockIdx.y;
+  const int g0 = split * ng / a.splits, g1 = (split + 1) * ng / a.splits;
 
   // one buffer resource over the whole packed layer; this wavefront's weight tiles are
   // addressed by wavefront-uniform (SGPR) offsets (tiles past the last one are clamped:
@@ -115,7 +119,7 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
   uint4 areg[A_VEC];
   uint4 ireg;
   auto load_a = [&](int g) {
-    const bool live = g < ng;
+    const bool live = g < g1;
     const uint32_t skip = live ? 0u : kNoLoad;
     const uint32_t soff = live ? static_cast<uint32_t>(g) * kGroup * 2 : 0u;
 #pragma unroll
@@ -136,7 +140,7 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
     uint32_t s[WN], z[WN];
   };
   auto load_b = [&](BRegs& b, int g) {
-    const bool live = g < ng;
+    const bool live = g < g1;
     const uint32_t skip = live ? 0u : kNoLoad;
     const uint32_t gg = live ? static_cast<uint32_t>(g) : 0u;
 #pragma unroll
@@ -196,17 +200,17 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
 
   // prologue: X'(0) in LDS buffer 0, X'(1) and B(0) in registers
   BRegs b0, b1;
-  load_a(0);
-  load_b(b0, 0);
+  load_a(g0);
+  load_b(b0, g0);
   store_a(0);
-  load_a(1);
+  load_a(g0 + 1);
   __syncthreads();
 
   // two groups per trip: g from buffer 0 / b0, g + 1 from buffer 1 / b1. While one group
   // is multiplied, the weights of the next are in flight and its X' goes into the other
   // LDS buffer; one barrier per group.
   // (sched_barrier keeps the scheduler from sinking the prefetches below the math)
-  for (int g = 0; g < ng; g += 2) {
+  for (int g = g0; g < g1; g += 2) {
     load_b(b1, g + 1);
     __builtin_amdgcn_sched_barrier(0);
     compute(b0, 0);
@@ -216,14 +220,16 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
     __syncthreads();
     load_b(b0, g + 2);
     __builtin_amdgcn_sched_barrier(0);
-    if (g + 1 < ng) compute(b1, 1);
+    if (g + 1 < g1) compute(b1, 1);
     store_a(0);
     load_a(g + 3);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   }
 
-  // epilogue: element q of acc[ms][j] is row 4 (l / 16) + q, column l % 16 of its tile
+  // epilogue: element q of acc[ms][j] is row 4 (l / 16) + q, column l % 16 of its tile;
+  // binary16 y, or with split K this split's float32 partial sums
+  float* part = a.part ? a.part + static_cast<int64_t>(split) * a.M * a.N : nullptr;
 #pragma unroll
   for (int ms = 0; ms < WM; ++ms) {
 #pragma unroll
@@ -233,12 +239,43 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
       for (int q = 0; q < 4; ++q) {
         const int m = m_blk + wm * WM * 16 + ms * 16 + 4 * p + q;
         if (m < a.M && n < a.N) {
-          a.y[static_cast<int64_t>(m) * a.N + n] =
-              __builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[ms][j][q]));
+          const int64_t o = static_cast<int64_t>(m) * a.N + n;
+          if (part) {
+            part[o] = acc[ms][j][q];
+          } else {
+            a.y[o] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[ms][j][q]));
+          }
         }
       }
     }
   }
+}
+
+// y = binary16(sum over the splits of the partial sums, in split order): deterministic.
+// Four outputs per thread; M * N is a multiple of 8.
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* part, int splits,
+                                                            int64_t mn, uint16_t* y) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i >= mn) return;
+  float4_t v = *reinterpret_cast<const float4_t*>(part + i);
+  for (int s = 1; s < splits; ++s) v += *reinterpret_cast<const float4_t*>(part + s * mn + i);
+  const half2_t lo = {static_cast<_Float16>(v[0]), static_cast<_Float16>(v[1])};
+  const half2_t hi = {static_cast<_Float16>(v[2]), static_cast<_Float16>(v[3])};
+  *reinterpret_cast<uint2*>(y + i) = make_uint2(as_u32(lo), as_u32(hi));
+}
+
+// Splits of K for a launch of `blocks` output blocks: enough workgroups to cover the
+// 256 CUs about twice when the output alone gives fewer than 256, each split at least two
+// groups, and the partial sums' traffic (written once, read once) no more than the
+// weights' bytes.
+int pick_splits(int64_t blocks, int64_t M, int64_t N, int64_t K, int n_groups) {
+  if (blocks >= 256) return 1;
+  int64_t s = (512 + blocks - 1) / blocks;
+  s = s < n_groups / 2 ? s : n_groups / 2;
+  const int64_t traffic_cap = K / (16 * M);  // 8 S M N <= N K / 2
+  s = s < traffic_cap ? s : traffic_cap;
+  s = s < 16 ? s : 16;
+  return s < 1 ? 1 : static_cast<int>(s);
 }
 
 template <int WAVES_M, int WM, int WN, int SCHED, bool ASYM>
@@ -256,8 +293,27 @@ hipError_t launch_tiles_fmt(GemmArgs a, hipStream_t st) {
   a.n_blocks_m = (a.M + BM - 1) / BM;
   a.n_blocks_n = (a.N + BN - 1) / BN;
   const unsigned blocks = static_cast<unsigned>(a.n_blocks_m) * static_cast<unsigned>(a.n_blocks_n);
-  hipLaunchKernelGGL((gemm_kernel<WAVES_M, WM, WN, SCHED, ASYM>), dim3(blocks), dim3(kGThreads), lds, st, a);
+  hipLaunchKernelGGL((gemm_kernel<WAVES_M, WM, WN, SCHED, ASYM>), dim3(blocks, a.splits),
+                     dim3(kGThreads), lds, st, a);
+  if (a.splits > 1) {
+    const int64_t mn = static_cast<int64_t>(a.M) * a.N;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(static_cast<unsigned>((mn / 4 + 255) / 256)),
+                       dim3(256), 0, st, a.part, a.splits, mn, a.y);
+  }
   return hipGetLastError();
+}
+
+// Output blocks of the default tiling for an M x N product (see launch_gemm).
+template <int WAVES_M, int WM, int WN>
+int64_t blocks_of(int64_t M, int64_t N) {
+  constexpr int BM = WAVES_M * WM * 16, BN = (4 / WAVES_M) * WN * 16;
+  return ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+}
+int64_t default_blocks(int64_t M, int64_t N, int64_t K) {
+  if (M <= 16) return blocks_of<1, 1, 2>(M, N);
+  if (M <= 64) return blocks_of<1, 4, 2>(M, N);
+  if (K >= 8192 || N >= 16384) return blocks_of<1, 8, 2>(M, N);
+  return blocks_of<1, 4, 4>(M, N);
 }
 
 template <int WAVES_M, int WM, int WN, int SCHED = 0>
@@ -268,11 +324,14 @@ hipError_t launch_tiles(GemmArgs a, hipStream_t st) {
 
 }  // namespace
 
-size_t gemm_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const int s = pick_splits(default_blocks(M, N, K), M, N, K, static_cast<int>(K / kGroup));
+  return s > 1 ? static_cast<size_t>(s) * M * N * sizeof(float) : 0;
+}
 
 hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
-                       int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y, void*, size_t,
-                       hipStream_t st) {
+                       int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y, void* ws,
+                       size_t ws_bytes, hipStream_t st) {
   const PackedLayout L = make_layout(N, K, kGroup, fmt);
   GemmArgs a;
   a.x = x;
@@ -287,12 +346,17 @@ hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* p
   a.K = static_cast<int>(K);
   a.n_groups = static_cast<int>(L.n_groups);
   a.n_tiles = static_cast<int>(L.n_tiles);
-  // AWQ_GEMM_TILE = "lds,<WM*10+WN>" selects the LDS-dequant kernel,
-  // "waves_m,wm,wn,sched" a register-fed tiling (for tuning sweeps)
+  // split K when the output blocks alone leave CUs idle and the caller gave a workspace
+  // for the partial sums (without one the product runs unsplit)
+  a.splits = 1;
+  a.part = nullptr;
+  const int want = pick_splits(default_blocks(M, N, K), M, N, K, a.n_groups);
+  if (want > 1 && ws != nullptr && ws_bytes >= static_cast<size_t>(want) * M * N * sizeof(float)) {
+    a.splits = want;
+    a.part = static_cast<float*>(ws);
+  }
+  // AWQ_GEMM_TILE = "waves_m,wm,wn,sched" selects another tiling (for tuning sweeps)
   const char* env = getenv("AWQ_GEMM_TILE");
-  int lcfg = 0;
-  if (env && sscanf(env, "lds,%d", &lcfg) == 1)
-    return launch_gemm_lds(x, inv_s_c, packed, M, N, K, fmt, y, lcfg, st);
   int wv = 0, wm = 0, wn = 0, sc = 0;
   if (env && sscanf(env, "%d,%d,%d,%d", &wv, &wm, &wn, &sc) == 4) {
     if (wv == 1 && wm == 4 && wn == 4 && sc == 0) return launch_tiles<1, 4, 4, 0>(a, st);
@@ -308,11 +372,14 @@ hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* p
     if (wv == 2 && wm == 4 && wn == 4 && sc == 0) return launch_tiles<2, 4, 4, 0>(a, st);
     if (wv == 1 && wm == 2 && wn == 4 && sc == 0) return launch_tiles<1, 2, 4, 0>(a, st);
     if (wv == 1 && wm == 1 && wn == 4 && sc == 0) return launch_tiles<1, 1, 4, 0>(a, st);
+    if (wv == 1 && wm == 1 && wn == 2 && sc == 0) return launch_tiles<1, 1, 2, 0>(a, st);
+    if (wv == 1 && wm == 1 && wn == 1 && sc == 0) return launch_tiles<1, 1, 1, 0>(a, st);
   }
   // Defaults from sweeps on MI355X: at M <= 64 the product is bound by streaming the
   // weights, and narrow 64 x 128 workgroup tiles give the most workgroups; at larger M a
   // 64 x 256 tile (each wavefront 64 x 64) runs best, or for long K or wide N a 128 x 128
   // tile (each wavefront 128 x 32), which dequantizes each weight fragment for 8 row tiles.
+  if (M <= 16) return launch_tiles<1, 1, 2>(a, st);
   if (M <= 64) return launch_tiles<1, 4, 2>(a, st);
   if (K >= 8192 || N >= 16384) return launch_tiles<1, 8, 2>(a, st);
   return launch_tiles<1, 4, 4>(a, st);

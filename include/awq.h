@@ -152,10 +152,14 @@ int awq_dequant(const void* w, const uint16_t* scales, const int32_t* qzeros,
                 uint16_t* w_out, hipStream_t stream);
 
 /*
- * Workspace bytes that awq_gemv / awq_gemm need for an M x N x K call. The kernels of
- * this version keep every partial sum inside a workgroup and need none (0 is
- * returned); the argument is part of the ABI so that a caller that provides a buffer
- * keeps working with versions that split K across workgroups.
+ * Workspace bytes for an M x N x K call of awq_gemv / awq_gemm (0: none used).
+ * awq_gemv keeps every partial sum inside a workgroup and uses none. awq_gemm splits K
+ * across workgroups when its output blocks alone would leave CUs idle (small M): the
+ * float32 partial sums [splits][M][N] go to the workspace and a second kernel adds
+ * them in split order. Every call that uses the workspace overwrites the part it
+ * uses, so it needs no initialisation; calls that share one workspace must be ordered
+ * (same stream). With a NULL workspace awq_gemm runs unsplit: same accuracy, slower at
+ * small M.
  */
 size_t awq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group);
 
@@ -187,7 +191,9 @@ int awq_gemv(const uint16_t* x, const uint16_t* inv_s_c, const void* packed, int
  * batches turn the product into a matrix-matrix multiply; section "Kernel Execution:
  * Marlin vs. ExLlamaV2 INT4 GEMM Micro-Architecture": weights are unpacked to
  * binary16 just before the matrix instruction). Same arguments, math and accuracy as
- * awq_gemv; the dequantized weights fed to the matrix cores are exactly W_d.
+ * awq_gemv; the dequantized weights fed to the matrix cores are exactly W_d. The
+ * split of K (see awq_workspace_bytes) depends only on M, N, K and whether a large
+ * enough workspace is given, so repeated calls give the same bits.
  * Errors: INVALID_ARG, UNSUPPORTED, MISALIGNED, WORKSPACE, HIP.
  */
 int awq_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* packed, int64_t M,

@@ -52,7 +52,10 @@ def test_sizes():
     assert awq.awq_repacked_bytes(64, 200) == 0           # K % 128 != 0
     assert awq.awq_repacked_bytes(64, 256, 64) == 0       # unsupported group
     assert awq.awq_workspace_bytes(0, 4096, 4096) == 0
-    assert awq.awq_workspace_bytes(1, 4096, 4096) == 0     # no split-K in this version
+    # split-K partial sums only where the output blocks alone leave CUs idle
+    assert awq.awq_workspace_bytes(16, 4096, 4096) % (16 * 4096 * 4) == 0
+    assert awq.awq_workspace_bytes(16, 4096, 4096) > 0
+    assert awq.awq_workspace_bytes(2048, 4096, 4096) == 0
 
 
 def test_padded_layout_size():

@@ -234,8 +234,12 @@ def test_gemv_parity(n, k, m, fmt):
 @pytest.mark.parametrize("n,k", [(512, 512), (200, 1024), (72, 256)])
 def test_gemm_parity(n, k, m, fmt):
     d, g, o, y_ref = product_case(n, k, m, fmt)
-    y = awq.awq_gemm(to_dev(d["x"]), g["inv"], g["packed"], n, k, 128, fmt)
+    x = to_dev(d["x"])
+    y = awq.awq_gemm(x, g["inv"], g["packed"], n, k, 128, fmt)           # unsplit
     assert rel_err(y.cpu().numpy(), y_ref) <= TOL
+    ws = awq.workspace(m, n, k, DEV)                                       # split K
+    y2 = awq.awq_gemm(x, g["inv"], g["packed"], n, k, 128, fmt, ws=ws)
+    assert rel_err(y2.cpu().numpy(), y_ref) <= TOL
 
 
 def test_products_with_prescaled_activations():
@@ -268,13 +272,14 @@ def test_m_zero_is_a_no_op():
     awq.awq_gemm(x, None, g["packed"], n, k, y=y)
 
 
-@pytest.mark.parametrize("fn", ["gemv", "gemm"])
-def test_products_deterministic(fn):
-    n, k, m = 4096, 4096, 1 if fn == "gemv" else 96
+@pytest.mark.parametrize("fn,m", [("gemv", 1), ("gemm", 96), ("gemm", 16)])
+def test_products_deterministic(fn, m):
+    n, k = 4096, 4096
     d, g, o, y_ref = product_case(n, k, m, 0)
     x = to_dev(d["x"])
     f = awq.awq_gemv if fn == "gemv" else awq.awq_gemm
-    ys = [f(x, g["inv"], g["packed"], n, k) for _ in range(5)]
+    ws = awq.workspace(m, n, k, DEV)     # M = 16: K split across workgroups
+    ys = [f(x, g["inv"], g["packed"], n, k, ws=ws) for _ in range(5)]
     torch.cuda.synchronize()
     for y in ys[1:]:
         assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
