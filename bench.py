@@ -10,9 +10,20 @@ enough copies of the weights (> 1 GB) that every step reads its weights from HBM
 from the 256 MB last-level cache.
 
 value = algorithmic bytes of a step (codes + scales + zeros + x + y + inv_s_c) / time.
-The same run times the prefill GEMM at M = 2048 on the Llama-3-8B shapes (4096 -> 6144,
-4096 -> 28672, 14336 -> 4096) and reports it under "gemm", and times the CPU oracle on a
-bounded sample of the decode workload under "cpu_baseline".
+
+Also reported (same JSON line):
+  per_layer_kernel  each decode shape alone, back-to-back launches in a graph;
+  fused_step        the same seven products as four launches (q|k|v as one 4096 -> 12288
+                    layer, gate|up as one 4096 -> 22016 layer), and the linear-layer
+                    token-rate bound of a 32-block 7B model at both step times;
+  batched           M = 8, 16, 32, 64 rows at 4096 -> 11008 (the GEMV -> matrix-core
+                    crossover);
+  llama70b_m1       8192 -> 28672 and 28672 -> 8192 at M = 1, asymmetric and symmetric;
+  gemm              the prefill GEMM at M = 2048 on the Llama-3-8B shapes (4096 -> 6144,
+                    4096 -> 28672, 14336 -> 4096);
+  unfused           awq_dequant to binary16 + the library fp16 GEMM (hipBLASLt through
+                    torch.matmul) at the same shapes: the unfused baseline;
+  cpu_baseline      the CPU oracle on a bounded sample of the decode workload.
 """
 from __future__ import annotations
 
@@ -31,8 +42,13 @@ DECODE_LAYERS = [  # (name, N, K)
     ("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),
     ("gate", 11008, 4096), ("up", 11008, 4096), ("down", 4096, 11008),
 ]
+FUSED_LAYERS = [("qkv", 12288, 4096), ("o", 4096, 4096), ("gate_up", 22016, 4096),
+                ("down", 4096, 11008)]
 PREFILL_LAYERS = [("qkv", 6144, 4096), ("gate_up", 28672, 4096), ("down", 4096, 14336)]
 PREFILL_M = 2048
+BATCHED_M = (8, 16, 32, 64)
+LAYERS_70B = [("up", 28672, 8192), ("down", 8192, 28672)]
+N_BLOCKS_7B = 32
 DOMINANT = "gate"  # 4096 -> 11008: the largest share of the step's kernel time
 
 
@@ -42,11 +58,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--rotate-bytes", type=float, default=1.2e9,
-                    help="total bytes of distinct weight copies the steps cycle through")
-    ap.add_argument("--no-gemm", action="store_true")
+                    help="total bytes of distinct weight copies the launches cycle through")
+    ap.add_argument("--no-gemm", action="store_true", help="skip prefill GEMM and unfused")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip fused step, batched decode and 70B layers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--gemm-iters", type=int, default=20)
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     return ap.parse_args()
@@ -63,7 +80,6 @@ def main():
               "multi-GPU runs are not part of this benchmark", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from bit_weight_only_w4a16_amd import awq, synth
@@ -75,36 +91,66 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    def make_layer(config, n, k, m=1, layer=0, fmt=awq.FMT_ASYM):
+        """Quantize a synthetic layer on the GPU (channel scale, pack, repack)."""
+        d = synth.layer_inputs(config, m, n, k, layer=layer)
+        w = torch.from_numpy(d["w"]).to(dev)
+        s_c, inv = awq.awq_channel_scale(torch.from_numpy(d["x_cal"]).to(dev), 0.5)
+        qw, sc, qz = awq.awq_pack(w, s_c, GROUP, fmt)
+        packed = awq.awq_repack(qw, sc, qz, n, k, GROUP, fmt)
+        del w, qw, sc, qz
+        return {"n": n, "k": k, "m": m, "fmt": fmt, "inv": inv, "packed": packed,
+                "x": torch.from_numpy(d["x"]).to(dev),
+                "y": torch.empty((m, n), dtype=torch.float16, device=dev)}
+
+    def rotation(weight_bytes):
+        return max(2, math.ceil(args.rotate_bytes / weight_bytes))
+
+    def graph_us(launches, reps, trials=3):
+        """Per-launch microseconds of a graph of back-to-back launches, replayed `reps`
+        times between two events on the capture stream; median of `trials`."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for f in launches:
+                f()
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(trials):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / (reps * len(launches)))
+        del g
+        return sorted(ts)[len(ts) // 2]
+
+    def product(fn, L, packed, ws):
+        return lambda: fn(L["x"], L["inv"], packed, L["n"], L["k"], GROUP, L["fmt"],
+                          y=L["y"], ws=ws)
+
     # ------------------------------------------------------------ decode layers
     log("quantizing the seven decode layers on the GPU")
     layers = []
     for j, (name, n, k) in enumerate(DECODE_LAYERS):
-        d = synth.layer_inputs(1, 1, n, k, layer=j)
-        w = torch.from_numpy(d["w"]).to(dev)
-        s_c, inv = awq.awq_channel_scale(torch.from_numpy(d["x_cal"]).to(dev), 0.5)
-        qw, sc, qz = awq.awq_pack(w, s_c)
-        packed = awq.awq_repack(qw, sc, qz, n, k)
-        del w, qw, sc, qz
-        layers.append({"name": name, "n": n, "k": k, "x": torch.from_numpy(d["x"]).to(dev),
-                       "inv": inv, "packed": packed,
-                       "y": torch.empty((1, n), dtype=torch.float16, device=dev),
-                       "bytes": rl.algorithmic_bytes(1, n, k, GROUP, rl.FMT_ASYM, with_inv=True)})
+        L = make_layer(1, n, k, layer=j)
+        L["name"] = name
+        L["bytes"] = rl.algorithmic_bytes(1, n, k, GROUP, rl.FMT_ASYM, with_inv=True)
+        layers.append(L)
     step_bytes = sum(L["bytes"] for L in layers)
     step_weight_bytes = sum(L["packed"].numel() for L in layers)
-    rot = max(2, math.ceil(args.rotate_bytes / step_weight_bytes))
+    rot = rotation(step_weight_bytes)
     copies = [[L["packed"]] + [L["packed"].clone() for _ in range(rot - 1)] for L in layers]
-    ws = awq.workspace(1, 11008, 11008, dev)
+    ws = None
     for L in layers:  # grow once to the largest need, before any capture
         ws = awq.workspace(1, L["n"], L["k"], dev)
 
-    def run_step(r, events=None):
+    def run_step(r):
         for j, L in enumerate(layers):
-            if events is not None:
-                events[j][0].record()
             awq.awq_gemv(L["x"], L["inv"], copies[j][r], L["n"], L["k"], GROUP, awq.FMT_ASYM,
                          y=L["y"], ws=ws)
-            if events is not None:
-                events[j][1].record()
 
     # warmup (eager) and graph capture: one graph per rotation copy, one for all copies
     for i in range(max(1, args.warmup)):
@@ -138,6 +184,7 @@ def main():
     t1 = time.perf_counter()
     sec = t1 - t0
     value_gbs = step_bytes * K / sec / 1e9
+    del g_all, g_one
 
     # ------------------------------------------- per-kernel durations (HIP events)
     # One graph per layer shape holding that layer's GEMV over all its weight copies,
@@ -147,70 +194,133 @@ def main():
     for shape_layer in ("q", "gate", "down"):
         j = next(i for i, L in enumerate(layers) if L["name"] == shape_layer)
         L = layers[j]
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for r in range(rot):
-                awq.awq_gemv(L["x"], L["inv"], copies[j][r], L["n"], L["k"], GROUP,
-                             awq.FMT_ASYM, y=L["y"], ws=ws)
-        g.replay()
-        torch.cuda.synchronize()
         reps = max(2, (8 * K) // (7 * rot))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (reps * rot)
+        us = graph_us([product(awq.awq_gemv, L, copies[j][r], ws) for r in range(rot)], reps)
         per_layer[shape_layer] = {"shape": f"{L['k']}->{L['n']}", "us": round(us, 3),
-                                  "GB/s": round(L["bytes"] / us / 1e3, 1), "launches": reps * rot}
-        del g
+                                  "GB/s": round(L["bytes"] / us / 1e3, 1),
+                                  "launches": 3 * reps * rot}
     dom = next(L for L in layers if L["name"] == DOMINANT)
     dom_us = per_layer[DOMINANT]["us"]
     achieved = dom["bytes"] / dom_us / 1e3  # GB/s
     sum_kernel_us = 4 * per_layer["q"]["us"] + 2 * per_layer["gate"]["us"] + per_layer["down"]["us"]
     traffic = measured_traffic(dom["bytes"])
+    del copies, layers
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if not args.no_extra:
+        # -------------------------------------- fused q|k|v and gate|up: four launches
+        log("fused decode step (4 launches)")
+        fl = [make_layer(1, n, k, layer=20 + j) for j, (_, n, k) in enumerate(FUSED_LAYERS)]
+        f_bytes = sum(rl.algorithmic_bytes(1, L["n"], L["k"], GROUP, rl.FMT_ASYM, True)
+                      for L in fl)
+        f_rot = rotation(sum(L["packed"].numel() for L in fl))
+        f_cp = [[L["packed"]] + [L["packed"].clone() for _ in range(f_rot - 1)] for L in fl]
+        for L in fl:
+            ws = awq.workspace(1, L["n"], L["k"], dev)
+        launches = [product(awq.awq_gemv, L, f_cp[j][r], ws)
+                    for r in range(f_rot) for j, L in enumerate(fl)]
+        f_us = graph_us(launches, max(2, K // f_rot)) * len(fl)  # per step
+        step_us = sec / K * 1e6
+        extra["fused_step"] = {
+            "launches": [f"{L['k']}->{L['n']}" for L in fl], "us_per_step": round(f_us, 3),
+            "GB/s": round(f_bytes / f_us / 1e3, 1),
+            "linear_tok_per_s_7b": {"7_launches": round(1e6 / (N_BLOCKS_7B * step_us), 1),
+                                    "4_launches": round(1e6 / (N_BLOCKS_7B * f_us), 1),
+                                    "bound_at_8TB/s": round(rl.max_tokens_per_s(
+                                        rl.HBM_PEAK_GBS, N_BLOCKS_7B * step_bytes / 1e9), 1)}}
+        del f_cp, fl, launches
+        torch.cuda.empty_cache()
+
+        # -------------------------------------- batched decode M = 8 .. 64, 4096 -> 11008
+        log("batched decode")
+        bl = make_layer(2, 11008, 4096, m=max(BATCHED_M))
+        b_rot = rotation(bl["packed"].numel())
+        b_cp = [bl["packed"]] + [bl["packed"].clone() for _ in range(b_rot - 1)]
+        xall = bl["x"]
+        batched = []
+        for m in BATCHED_M:
+            L = dict(bl, m=m, x=xall[:m].contiguous(),
+                     y=torch.empty((m, bl["n"]), dtype=torch.float16, device=dev))
+            ws = awq.workspace(m, L["n"], L["k"], dev)
+            fn, name = (awq.awq_gemv, "awq_gemv") if m <= 8 else (awq.awq_gemm, "awq_gemm")
+            us = graph_us([product(fn, L, b_cp[r], ws) for r in range(b_rot)], 10)
+            byts = rl.algorithmic_bytes(m, L["n"], L["k"], GROUP, rl.FMT_ASYM, True)
+            batched.append({"M": m, "entry": name, "us": round(us, 3),
+                            "GB/s": round(byts / us / 1e3, 1),
+                            "TFLOP/s": round(rl.flops(m, L["n"], L["k"]) / us / 1e6, 2)})
+        extra["batched"] = {"shape": "4096->11008", "rows": batched}
+        del b_cp, bl, xall
+        torch.cuda.empty_cache()
+
+        # -------------------------------------- 70B layers at M = 1
+        log("70B layers at M = 1")
+        rows70 = []
+        for fmt, fname in ((awq.FMT_ASYM, "asym"), (awq.FMT_SYM8, "sym")):
+            for j, (name, n, k) in enumerate(LAYERS_70B):
+                L = make_layer(4, n, k, layer=j, fmt=fmt)
+                r70 = rotation(L["packed"].numel())
+                cp = [L["packed"]] + [L["packed"].clone() for _ in range(r70 - 1)]
+                ws = awq.workspace(1, n, k, dev)
+                us = graph_us([product(awq.awq_gemv, L, cp[r], ws) for r in range(r70)], 5)
+                byts = rl.algorithmic_bytes(1, n, k, GROUP, fmt, True)
+                rows70.append({"layer": name, "shape": f"{k}->{n}", "format": fname,
+                               "us": round(us, 3), "GB/s": round(byts / us / 1e3, 1),
+                               "frac": round(byts / us / 1e3 / rl.HBM_PEAK_GBS, 4)})
+                del cp, L
+                torch.cuda.empty_cache()
+        extra["llama70b_m1"] = rows70
 
     # ------------------------------------------------------------ prefill GEMM
-    gemm = None
+    gemm = unfused = None
     if not args.no_gemm:
         log("prefill GEMM M=2048")
-        del copies, g_all, g_one
-        torch.cuda.empty_cache()
         gl = []
+        ul = []
         tot_flop = tot_us = 0.0
         for j, (name, n, k) in enumerate(PREFILL_LAYERS):
-            d = synth.layer_inputs(3, PREFILL_M, n, k, layer=j)
-            w = torch.from_numpy(d["w"]).to(dev)
-            s_c, inv = awq.awq_channel_scale(torch.from_numpy(d["x_cal"]).to(dev), 0.5)
-            qw, sc, qz = awq.awq_pack(w, s_c)
-            packed = awq.awq_repack(qw, sc, qz, n, k)
-            del w, qw, sc, qz
-            x = torch.from_numpy(d["x"]).to(dev)
-            y = torch.empty((PREFILL_M, n), dtype=torch.float16, device=dev)
-            for _ in range(3):
-                awq.awq_gemm(x, inv, packed, n, k, y=y)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            e0.record()
-            for _ in range(args.gemm_iters):
-                awq.awq_gemm(x, inv, packed, n, k, y=y)
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / args.gemm_iters
+            L = make_layer(3, n, k, m=PREFILL_M, layer=j)
+            cp = [L["packed"], L["packed"].clone()]
+            ws = awq.workspace(PREFILL_M, n, k, dev)
+            us = graph_us([product(awq.awq_gemm, L, cp[r % 2], ws) for r in range(6)], 3)
             fl = rl.flops(PREFILL_M, n, k)
             tot_flop += fl
             tot_us += us
             gl.append({"shape": f"{k}->{n}", "M": PREFILL_M, "us": round(us, 2),
                        "TFLOP/s": round(fl / us / 1e6, 1),
                        "frac": round(fl / us / 1e6 / rl.MFMA_F16_PEAK_TFLOPS, 4)})
-            del packed, x, y
+            # unfused baseline: dequantize to binary16, then the library fp16 GEMM
+            xs = (L["x"].float() * L["inv"].float()).half()  # X' as the fused path forms it
+            wd = torch.empty((n, k), dtype=torch.float16, device=dev)
+
+            def unfused_call():
+                awq.awq_dequant(L["packed"], None, None, awq.LAYOUT_GFX950, n, k, GROUP,
+                                awq.FMT_ASYM, out=wd)
+                torch.matmul(xs, wd.t(), out=L["y"])
+
+            for _ in range(2):
+                unfused_call()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                unfused_call()
+            e1.record()
+            torch.cuda.synchronize()
+            u_us = e0.elapsed_time(e1) * 1e3 / 5
+            ul.append({"shape": f"{k}->{n}", "M": PREFILL_M, "us": round(u_us, 2),
+                       "TFLOP/s": round(fl / u_us / 1e6, 1),
+                       "fused_speedup": round(u_us / us, 3)})
+            del L, cp, xs, wd
+            torch.cuda.empty_cache()
         agg = tot_flop / tot_us / 1e6
         gemm = {"workload": "llama3_8b_prefill_m2048", "metric": "TFLOP/s", "value": round(agg, 1),
                 "roofline": {"bound": "mfma", "achieved": round(agg, 1),
                              "peak": round(rl.MFMA_F16_PEAK_TFLOPS, 1), "unit": "TFLOP/s",
                              "frac": round(agg / rl.MFMA_F16_PEAK_TFLOPS, 4)},
                 "layers": gl}
+        unfused = {"what": "awq_dequant to binary16 W_d, then torch.matmul (hipBLASLt fp16)",
+                   "prefill": ul}
 
     if args.copy_probe:
         a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -250,7 +360,9 @@ def main():
         "per_layer_kernel": per_layer,
         "kernel_sum_us_per_step": round(sum_kernel_us, 3),
         "kernel_only_GB/s": round(step_bytes / sum_kernel_us / 1e3, 1),
+        **extra,
         "gemm": gemm,
+        "unfused": unfused,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -290,8 +402,6 @@ def measured_traffic(algorithmic_bytes: int):
 
 def cpu_baseline(seconds: float):
     """The CPU oracle (as it stands) on the dominant decode layer: dequantize + product."""
-    import numpy as np
-
     import oracle
     from bit_weight_only_w4a16_amd import synth
     from bit_weight_only_w4a16_amd import roofline as rl
