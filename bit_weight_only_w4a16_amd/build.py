@@ -45,6 +45,7 @@ def hipcc() -> str:
 FILE_FLAGS = {
     "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gemm_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

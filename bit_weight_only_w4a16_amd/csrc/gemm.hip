@@ -324,7 +324,12 @@ hipError_t launch_tiles(GemmArgs a, hipStream_t st) {
 
 }  // namespace
 
+// Large M runs the wide-tile kernel, which needs X' in the workspace when inv_s_c is
+// given.
+constexpr int64_t kWideMinM = 256;
+
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M >= kWideMinM) return gemm_wide_workspace_bytes(M, K);
   const int s = pick_splits(default_blocks(M, N, K), M, N, K, static_cast<int>(K / kGroup));
   return s > 1 ? static_cast<size_t>(s) * M * N * sizeof(float) : 0;
 }
@@ -332,6 +337,16 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
                        int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y, void* ws,
                        size_t ws_bytes, hipStream_t st) {
+  // large M: wide wavefront tiles, X' from the workspace (or pre-scaled by the caller);
+  // AWQ_GEMM_WIDE = "0" keeps the narrow kernel, "2" / "4" forces the column tiles
+  // per wavefront (for tuning sweeps)
+  const char* wide = getenv("AWQ_GEMM_WIDE");
+  const bool wide_ok = inv_s_c == nullptr || (ws != nullptr && ws_bytes >= gemm_wide_workspace_bytes(M, K));
+  if (M >= kWideMinM && wide_ok && !(wide && wide[0] == '0')) {
+    int wn = 4;
+    if (wide && (wide[0] == '2' || wide[0] == '4')) wn = wide[0] - '0';
+    return launch_gemm_wide(x, inv_s_c, packed, M, N, K, fmt, y, ws, wn, st);
+  }
   const PackedLayout L = make_layout(N, K, kGroup, fmt);
   GemmArgs a;
   a.x = x;

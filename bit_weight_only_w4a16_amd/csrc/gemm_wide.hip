@@ -1,0 +1,269 @@
+// Prefill product y[M, N] = X' . deq(Wq)^T for large M on the gfx950 matrix cores, with
+// wide wavefront tiles.
+//
+// Prefill is bound by matrix-core throughput (edgesiliconlab ?p=2015, section "GEMM vs.
+// GEMV Kernels and Batch Size Dynamics"); the weights are turned into binary16 in
+// registers right before the matrix instruction (same page, section "Kernel Execution:
+// Marlin vs. ExLlamaV2 INT4 GEMM Micro-Architecture", item 3), exactly
+// W_d = binary16((q - z) * s). Three resources compete per 128-channel group: the
+// matrix core, the VALU work of that dequantization (13 instructions per 8 weights),
+// and LDS bandwidth for the activation operand. A wavefront tile of 128 rows x 64
+// columns (8 x 4 matrix-core tiles of 16 x 16) reuses each dequantized weight fragment
+// for 8 row tiles and each activation fragment for 4 column tiles, which keeps the
+// dequantization near 40 % and the LDS reads near 50 % of the matrix-core time.
+//
+//  * X' = binary16(X * inv_s_c) is formed once per call by `prescale_kernel` (into the
+//    caller's workspace) or passed in pre-scaled, so the activation tile can go from
+//    memory straight into LDS: `buffer_load_dwordx4 ... lds` writes each lane's 16 bytes
+//    at LDS base + 16 * lane, no registers involved. Rows are 256 bytes with no padding;
+//    16-byte chunk c of row r is stored at chunk position c ^ (r % 16) (the lanes pick
+//    their global chunk accordingly), so the 16 rows read by one matrix-core fragment
+//    load fall in 16 different bank groups.
+//  * Activation tiles are double-buffered in LDS (2 x 32 KiB), one barrier per group; the
+//    weights of the next group are in registers while a group is multiplied; every load
+//    is issued unconditionally (a group past the end reads zeros).
+//  * Four wavefronts side by side along N: a workgroup covers 128 x 256 outputs (or
+//    128 x 128 with two column tiles per wavefront); accumulators in VGPRs.
+#include "awq_internal.hpp"
+
+namespace awq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBM = 128;              // rows of X' per workgroup
+constexpr int kRowBytes = kGroup * 2;  // one activation row of a group: 256 B
+constexpr int kTileBytes = kBM * kRowBytes;
+constexpr int kXcds = 8;
+
+struct WideArgs {
+  const uint16_t* xs;  // X' [M][K] binary16
+  const uint8_t* packed;
+  uint16_t* y;
+  int64_t scales_off;
+  int64_t zeros_off;
+  uint32_t packed_bytes;
+  int M, N, K, n_groups, n_tiles, n_blocks_m, n_blocks_n;
+};
+
+__global__ void __launch_bounds__(256) prescale_kernel(const uint16_t* x, const uint16_t* inv,
+                                                       int64_t total, int K, uint16_t* xs) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (i >= total) return;
+  const uint4 xv = *reinterpret_cast<const uint4*>(x + i);
+  const uint4 iv = *reinterpret_cast<const uint4*>(inv + i % K);
+  *reinterpret_cast<uint4*>(xs + i) = scale_x8(xv, iv);
+}
+
+template <int WN, bool ASYM>
+__global__ void __launch_bounds__(kThreads) gemm_wide_kernel(WideArgs a) {
+  constexpr int WM = 8;
+  constexpr int BN = 4 * WN * 16;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];  // [2][kBM][256 B]
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, p = lane >> 4;
+
+  const int nb = a.n_blocks_m * a.n_blocks_n;
+  int bid = blockIdx.x;
+  if (nb % kXcds == 0) bid = (bid % kXcds) * (nb / kXcds) + bid / kXcds;
+  const int bm = bid % a.n_blocks_m, bn = bid / a.n_blocks_m;
+  const int m_blk = bm * kBM, n_blk = bn * BN;
+  const int ng = a.n_groups;
+
+  // weights: one resource over the packed layer, per-tile SGPR offsets (tiles past the
+  // last are clamped: their outputs are never stored)
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.packed, a.packed_bytes);
+  uint32_t code_off[WN], scale_off[WN], zero_off[WN];
+#pragma unroll
+  for (int j = 0; j < WN; ++j) {
+    const uint32_t tile = static_cast<uint32_t>(min(n_blk / kTileN + wave * WN + j, a.n_tiles - 1));
+    code_off[j] = tile * ng * kUnitBytes;
+    scale_off[j] = static_cast<uint32_t>(a.scales_off) + tile * ng * (2 * kTileN);
+    zero_off[j] = ASYM ? static_cast<uint32_t>(a.zeros_off) + tile * ng * 8 : 0u;
+  }
+  const uint32_t lane_code = 16u * lane, lane_scale = 2u * r, lane_zero = 4u * (r >> 3);
+  const int zshift = 4 * (r & 7);
+
+  // activations: this block's rows (rows past M read as 0). Wavefront w fills LDS rows
+  // 32 w .. 32 w + 31 of a buffer with 8 instructions of 4 rows each; lane l of
+  // instruction j writes row 32 w + 4 j + l / 16, chunk position l % 16, which holds the
+  // global chunk (l % 16) ^ (row % 16).
+  const int rows_here = min(kBM, a.M - m_blk);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.xs + static_cast<int64_t>(m_blk) * a.K,
+                                              static_cast<uint32_t>(rows_here) * a.K * 2);
+  uint32_t a_voff[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = 32 * wave + 4 * j + (lane >> 4);
+    const int chunk = (lane & 15) ^ (row & 15);
+    a_voff[j] = static_cast<uint32_t>(row * a.K + 8 * chunk) * 2;
+  }
+  auto dma_a = [&](int g, int buf) {
+    const bool live = g < ng;
+    const uint32_t skip = live ? 0u : kNoLoad;
+    const int soff = live ? g * kRowBytes : 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      unsigned char* dst = smem + buf * kTileBytes + (32 * wave + 4 * j) * kRowBytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (__attribute__((address_space(3))) void*)(dst), 16,
+          static_cast<int>(a_voff[j] + skip), __builtin_amdgcn_readfirstlane(soff), 0, 0);
+    }
+  };
+
+  struct BRegs {
+    uint4 c[WN];
+    uint32_t s[WN], z[WN];
+  };
+  auto load_b = [&](BRegs& b, int g) {
+    const bool live = g < ng;
+    const uint32_t skip = live ? 0u : kNoLoad;
+    const uint32_t gg = live ? static_cast<uint32_t>(g) : 0u;
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      b.c[j] = buf_load16(rp, lane_code + skip, code_off[j] + gg * kUnitBytes);
+      b.s[j] = buf_load2(rp, lane_scale + skip, scale_off[j] + gg * (2 * kTileN));
+      if (ASYM) b.z[j] = buf_load4(rp, lane_zero + skip, zero_off[j] + gg * 8);
+    }
+  };
+
+  float4_t acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) acc[i][j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](const BRegs& b, int buf) {
+    const unsigned char* src = smem + buf * kTileBytes;
+    half2_t s2[WN];
+    uint32_t nz1024[WN], nz64[WN];
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      const uint32_t z = ASYM ? (b.z[j] >> zshift) & 0xFu : 8u;
+      s2[j] = as_h2(b.s[j] | (b.s[j] << 16));
+      nz1024[j] = neg_off1024(z);
+      nz64[j] = neg_off64(z);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      half8_t bf[WN];
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const uint32_t w = i == 0 ? b.c[j].x : i == 1 ? b.c[j].y : i == 2 ? b.c[j].z : b.c[j].w;
+        half2_t d[4];
+        dequant_word(w, nz1024[j], nz64[j], s2[j], d);
+        bf[j] = half8_t{d[0].x, d[0].y, d[1].x, d[1].y, d[2].x, d[2].y, d[3].x, d[3].y};
+      }
+      // A fragment of row tile ms, k-step i: row 16 ms + r, chunk 4 p + i (swizzled)
+      const int chunk = (4 * p + i) ^ r;
+#pragma unroll
+      for (int ms = 0; ms < WM; ++ms) {
+        const half8_t af = *reinterpret_cast<const half8_t*>(src + (16 * ms + r) * kRowBytes + 16 * chunk);
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          acc[ms][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[j], acc[ms][j], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // prologue: A(0) in LDS buffer 0, B(0) in registers
+  BRegs b0, b1;
+  dma_a(0, 0);
+  load_b(b0, 0);
+  __builtin_amdgcn_s_waitcnt(0);  // the A(0) transfers have landed
+  __syncthreads();
+
+  // two groups per trip; while group g is multiplied from one buffer, A(g + 1) streams
+  // into the other and B(g + 1) into registers; one barrier per group
+  for (int g = 0; g < ng; g += 2) {
+    dma_a(g + 1, 1);
+    load_b(b1, g + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    dma_a(g + 2, 0);
+    load_b(b0, g + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (g + 1 < ng) compute(b1, 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int ms = 0; ms < WM; ++ms) {
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      const int n = n_blk + (wave * WN + j) * 16 + r;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = m_blk + ms * 16 + 4 * p + q;
+        if (m < a.M && n < a.N) {
+          a.y[static_cast<int64_t>(m) * a.N + n] =
+              __builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[ms][j][q]));
+        }
+      }
+    }
+  }
+}
+
+template <int WN, bool ASYM>
+hipError_t launch_wide_fmt(WideArgs a, hipStream_t st) {
+  constexpr int BN = 4 * WN * 16;
+  const size_t lds = 2ull * kTileBytes;
+  static bool attr_set = false;  // benign race: every thread sets the same value
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_wide_kernel<WN, ASYM>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  a.n_blocks_m = (a.M + kBM - 1) / kBM;
+  a.n_blocks_n = (a.N + BN - 1) / BN;
+  const unsigned blocks = static_cast<unsigned>(a.n_blocks_m) * static_cast<unsigned>(a.n_blocks_n);
+  hipLaunchKernelGGL((gemm_wide_kernel<WN, ASYM>), dim3(blocks), dim3(kThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t gemm_wide_workspace_bytes(int64_t M, int64_t K) {
+  return static_cast<size_t>(M) * K * sizeof(uint16_t);
+}
+
+// X' into the workspace when inv_s_c is given (ws must hold M * K binary16), then the
+// product; wn selects 4 (128 x 256 workgroup tiles) or 2 (128 x 128) column tiles per
+// wavefront.
+hipError_t launch_gemm_wide(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
+                            int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y,
+                            void* ws, int wn, hipStream_t st) {
+  const PackedLayout L = make_layout(N, K, kGroup, fmt);
+  const uint16_t* xs = x;
+  if (inv_s_c != nullptr) {
+    uint16_t* dst = static_cast<uint16_t*>(ws);
+    const int64_t total = M * K;
+    hipLaunchKernelGGL(prescale_kernel, dim3(static_cast<unsigned>((total / 8 + 255) / 256)),
+                       dim3(256), 0, st, x, inv_s_c, total, static_cast<int>(K), dst);
+    xs = dst;
+  }
+  WideArgs a;
+  a.xs = xs;
+  a.packed = static_cast<const uint8_t*>(packed);
+  a.y = y;
+  a.scales_off = L.scales_off;
+  a.zeros_off = L.zeros_off;
+  a.packed_bytes = static_cast<uint32_t>(L.total_bytes);
+  a.M = static_cast<int>(M);
+  a.N = static_cast<int>(N);
+  a.K = static_cast<int>(K);
+  a.n_groups = static_cast<int>(L.n_groups);
+  a.n_tiles = static_cast<int>(L.n_tiles);
+  const bool asym = L.zeros_off >= 0;
+  if (wn == 4) return asym ? launch_wide_fmt<4, true>(a, st) : launch_wide_fmt<4, false>(a, st);
+  return asym ? launch_wide_fmt<2, true>(a, st) : launch_wide_fmt<2, false>(a, st);
+}
+
+}  // namespace awq

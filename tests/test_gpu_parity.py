@@ -230,7 +230,7 @@ def test_gemv_parity(n, k, m, fmt):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
-@pytest.mark.parametrize("m", [1, 7, 16, 33, 64, 130])
+@pytest.mark.parametrize("m", [1, 7, 16, 33, 64, 130, 256, 300])
 @pytest.mark.parametrize("n,k", [(512, 512), (200, 1024), (72, 256)])
 def test_gemm_parity(n, k, m, fmt):
     d, g, o, y_ref = product_case(n, k, m, fmt)
@@ -242,15 +242,18 @@ def test_gemm_parity(n, k, m, fmt):
     assert rel_err(y2.cpu().numpy(), y_ref) <= TOL
 
 
-def test_products_with_prescaled_activations():
+@pytest.mark.parametrize("m", [3, 300])
+def test_products_with_prescaled_activations(m):
     """inv_s_c NULL: the caller passes X' = X * inv_s_c already in binary16."""
-    n, k, m = 256, 1024, 3
+    n, k = 256, 1024
     d, g, o, _ = product_case(n, k, m, 0)
     xs = oracle.fp16_rn(oracle.as_f64(d["x"]) * o["inv"][None, :]).astype(np.float16)
     y_ref = oracle.matmul_ref(xs, o["w_d"])
-    for fn in (awq.awq_gemv, awq.awq_gemm):
-        y = fn(to_dev(xs), None, g["packed"], n, k, 128, 0, ws=awq.workspace(m, n, k, DEV))
-        assert rel_err(y.cpu().numpy(), y_ref) <= TOL
+    fns = (awq.awq_gemv, awq.awq_gemm) if m <= 16 else (awq.awq_gemm,)
+    for fn in fns:
+        for ws in (awq.workspace(m, n, k, DEV), None):
+            y = fn(to_dev(xs), None, g["packed"], n, k, 128, 0, ws=ws)
+            assert rel_err(y.cpu().numpy(), y_ref) <= TOL
 
 
 def test_zero_weights_give_zero_output():
@@ -272,7 +275,7 @@ def test_m_zero_is_a_no_op():
     awq.awq_gemm(x, None, g["packed"], n, k, y=y)
 
 
-@pytest.mark.parametrize("fn,m", [("gemv", 1), ("gemm", 96), ("gemm", 16)])
+@pytest.mark.parametrize("fn,m", [("gemv", 1), ("gemm", 96), ("gemm", 16), ("gemm", 512)])
 def test_products_deterministic(fn, m):
     n, k = 4096, 4096
     d, g, o, y_ref = product_case(n, k, m, 0)
