@@ -153,13 +153,16 @@ int awq_dequant(const void* w, const uint16_t* scales, const int32_t* qzeros,
 
 /*
  * Workspace bytes for an M x N x K call of awq_gemv / awq_gemm (0: none used).
- * awq_gemv keeps every partial sum inside a workgroup and uses none. awq_gemm splits K
- * across workgroups when its output blocks alone would leave CUs idle (small M): the
- * float32 partial sums [splits][M][N] go to the workspace and a second kernel adds
- * them in split order. Every call that uses the workspace overwrites the part it
- * uses, so it needs no initialisation; calls that share one workspace must be ordered
- * (same stream). With a NULL workspace awq_gemm runs unsplit: same accuracy, slower at
- * small M.
+ * awq_gemv keeps every partial sum inside a workgroup and uses none. awq_gemm uses it
+ *  - at small M, when its output blocks alone would leave CUs idle: K is split across
+ *    workgroups, the float32 partial sums [splits][M][N] go to the workspace and a
+ *    second kernel adds them in split order;
+ *  - at M >= 256 with inv_s_c given: X' = binary16(X * inv_s_c) is formed once into the
+ *    workspace ([M][K] binary16) and the wide-tile kernel streams it into LDS.
+ * Every call that uses the workspace overwrites the part it uses, so it needs no
+ * initialisation; calls that share one workspace must be ordered (same stream). With a
+ * NULL workspace awq_gemm runs unsplit and scales X' inside the kernel: same accuracy,
+ * slower.
  */
 size_t awq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group);
 
