@@ -49,6 +49,7 @@ PREFILL_M = 2048
 BATCHED_M = (8, 16, 32, 64)
 LAYERS_70B = [("up", 28672, 8192), ("down", 8192, 28672)]
 N_BLOCKS_7B = 32
+GEMV_MAX_M = 4  # above this the split-K matrix-core GEMM is faster (batched rows)
 DOMINANT = "gate"  # 4096 -> 11008: the largest share of the step's kernel time
 
 
@@ -243,7 +244,7 @@ def main():
             L = dict(bl, m=m, x=xall[:m].contiguous(),
                      y=torch.empty((m, bl["n"]), dtype=torch.float16, device=dev))
             ws = awq.workspace(m, L["n"], L["k"], dev)
-            fn, name = (awq.awq_gemv, "awq_gemv") if m <= 8 else (awq.awq_gemm, "awq_gemm")
+            fn, name = (awq.awq_gemv, "awq_gemv") if m <= GEMV_MAX_M else (awq.awq_gemm, "awq_gemm")
             us = graph_us([product(fn, L, b_cp[r], ws) for r in range(b_rot)], 10)
             byts = rl.algorithmic_bytes(m, L["n"], L["k"], GROUP, rl.FMT_ASYM, True)
             batched.append({"M": m, "entry": name, "us": round(us, 3),

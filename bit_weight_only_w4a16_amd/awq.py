@@ -220,10 +220,11 @@ class QuantLinear:
 
     Built from fp16 weights with ``QuantLinear.from_weight`` (channel scale from
     calibration rows, fold, quantize, pack, repack -- all in the library's kernels).
-    Calls go to awq_gemv for M <= gemv_max_m rows and to awq_gemm above.
+    Calls go to awq_gemv for M <= gemv_max_m rows and to awq_gemm above (on MI355X the
+    split-K GEMM overtakes the decode kernel between 4 and 8 rows).
     """
 
-    def __init__(self, packed, n, k, inv_s_c=None, group=GROUP, fmt=FMT_ASYM, gemv_max_m=8):
+    def __init__(self, packed, n, k, inv_s_c=None, group=GROUP, fmt=FMT_ASYM, gemv_max_m=4):
         self.packed, self.n, self.k = packed, n, k
         self.inv_s_c, self.group, self.fmt = inv_s_c, group, fmt
         self.gemv_max_m = gemv_max_m

@@ -64,7 +64,7 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 size_t gemm_wide_workspace_bytes(int64_t M, int64_t K);
 hipError_t launch_gemm_wide(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
                             int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y,
-                            void* ws, int wn, hipStream_t st);
+                            void* ws, int cfg, hipStream_t st);
 hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
                        int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y, void* ws,
                        size_t ws_bytes, hipStream_t st);

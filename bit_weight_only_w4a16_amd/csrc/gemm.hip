@@ -338,14 +338,13 @@ hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* p
                        int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y, void* ws,
                        size_t ws_bytes, hipStream_t st) {
   // large M: wide wavefront tiles, X' from the workspace (or pre-scaled by the caller);
-  // AWQ_GEMM_WIDE = "0" keeps the narrow kernel, "2" / "4" forces the column tiles
-  // per wavefront (for tuning sweeps)
+  // AWQ_GEMM_WIDE = "0" keeps the narrow kernel, "<column tiles><K split>" (41, 42, 31,
+  // 32, 21, 22) forces a wide configuration (for tuning sweeps)
   const char* wide = getenv("AWQ_GEMM_WIDE");
   const bool wide_ok = inv_s_c == nullptr || (ws != nullptr && ws_bytes >= gemm_wide_workspace_bytes(M, K));
   if (M >= kWideMinM && wide_ok && !(wide && wide[0] == '0')) {
-    int wn = 4;
-    if (wide && (wide[0] == '2' || wide[0] == '4')) wn = wide[0] - '0';
-    return launch_gemm_wide(x, inv_s_c, packed, M, N, K, fmt, y, ws, wn, st);
+    const int cfg = wide ? atoi(wide) : 0;
+    return launch_gemm_wide(x, inv_s_c, packed, M, N, K, fmt, y, ws, cfg, st);
   }
   const PackedLayout L = make_layout(N, K, kGroup, fmt);
   GemmArgs a;

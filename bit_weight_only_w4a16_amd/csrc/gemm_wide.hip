@@ -23,13 +23,13 @@
 //    weights of the next group are in registers while a group is multiplied; every load
 //    is issued unconditionally (a group past the end reads zeros).
 //  * Four wavefronts side by side along N: a workgroup covers 128 x 256 outputs (or
-//    128 x 128 with two column tiles per wavefront); accumulators in VGPRs.
+//    128 x 192 / 128 x 128 with three / two column tiles per wavefront); accumulators in
+//    VGPRs. With few output blocks, eight wavefronts split K in two (see KS below).
 #include "awq_internal.hpp"
 
 namespace awq {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kBM = 128;              // rows of X' per workgroup
 constexpr int kRowBytes = kGroup * 2;  // one activation row of a group: 256 B
 constexpr int kTileBytes = kBM * kRowBytes;
@@ -54,13 +54,20 @@ __global__ void __launch_bounds__(256) prescale_kernel(const uint16_t* x, const 
   *reinterpret_cast<uint4*>(xs + i) = scale_x8(xv, iv);
 }
 
-template <int WN, bool ASYM>
-__global__ void __launch_bounds__(kThreads) gemm_wide_kernel(WideArgs a) {
+// KS = 2 splits K inside the workgroup: wavefronts 4..7 take the second half of the
+// groups with their own pair of LDS buffers, and add their sums to those of wavefronts
+// 0..3 through LDS at the end (in a fixed order), which gives two wavefronts per SIMD
+// when there are too few output blocks to fill the CUs twice.
+template <int WN, int KS, bool ASYM>
+__global__ void __launch_bounds__(256 * KS) gemm_wide_kernel(WideArgs a) {
   constexpr int WM = 8;
   constexpr int BN = 4 * WN * 16;
-  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];  // [2][kBM][256 B]
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem_all[];  // [KS][2][kBM][256 B]
 
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = wave_all >> 2;        // which part of K
+  const int wave = wave_all & 3;          // column slot within the workgroup
+  unsigned char* smem = smem_all + half * 2 * kTileBytes;
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, p = lane >> 4;
 
@@ -70,6 +77,10 @@ __global__ void __launch_bounds__(kThreads) gemm_wide_kernel(WideArgs a) {
   const int bm = bid % a.n_blocks_m, bn = bid / a.n_blocks_m;
   const int m_blk = bm * kBM, n_blk = bn * BN;
   const int ng = a.n_groups;
+  // this wavefront's groups [g0, g1); both halves run the same number of trips
+  const int g0 = half * ((a.n_groups + 1) / 2);
+  const int g1 = KS == 1 ? a.n_groups : min(a.n_groups, g0 + (a.n_groups + 1) / 2);
+  const int trips = KS == 1 ? a.n_groups : (a.n_groups + 1) / 2;
 
   // weights: one resource over the packed layer, per-tile SGPR offsets (tiles past the
   // last are clamped: their outputs are never stored)
@@ -100,7 +111,7 @@ __global__ void __launch_bounds__(kThreads) gemm_wide_kernel(WideArgs a) {
     a_voff[j] = static_cast<uint32_t>(row * a.K + 8 * chunk) * 2;
   }
   auto dma_a = [&](int g, int buf) {
-    const bool live = g < ng;
+    const bool live = g < g1;
     const uint32_t skip = live ? 0u : kNoLoad;
     const int soff = live ? g * kRowBytes : 0;
 #pragma unroll
@@ -117,7 +128,7 @@ __global__ void __launch_bounds__(kThreads) gemm_wide_kernel(WideArgs a) {
     uint32_t s[WN], z[WN];
   };
   auto load_b = [&](BRegs& b, int g) {
-    const bool live = g < ng;
+    const bool live = g < g1;
     const uint32_t skip = live ? 0u : kNoLoad;
     const uint32_t gg = live ? static_cast<uint32_t>(g) : 0u;
 #pragma unroll
@@ -170,26 +181,48 @@ __global__ void __launch_bounds__(kThreads) gemm_wide_kernel(WideArgs a) {
 
   // prologue: A(0) in LDS buffer 0, B(0) in registers
   BRegs b0, b1;
-  dma_a(0, 0);
-  load_b(b0, 0);
-  __builtin_amdgcn_s_waitcnt(0);  // the A(0) transfers have landed
+  dma_a(g0, 0);
+  load_b(b0, g0);
+  __builtin_amdgcn_s_waitcnt(0);  // the A(g0) transfers have landed
   __syncthreads();
 
   // two groups per trip; while group g is multiplied from one buffer, A(g + 1) streams
-  // into the other and B(g + 1) into registers; one barrier per group
-  for (int g = 0; g < ng; g += 2) {
+  // into the other and B(g + 1) into registers; one barrier per group (every wavefront
+  // of the workgroup takes the same number of trips, so the barriers match)
+  for (int t = 0; t < trips; t += 2) {
+    const int g = g0 + t;
     dma_a(g + 1, 1);
     load_b(b1, g + 1);
     __builtin_amdgcn_sched_barrier(0);
-    compute(b0, 0);
+    if (g < g1) compute(b0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     dma_a(g + 2, 0);
     load_b(b0, g + 2);
     __builtin_amdgcn_sched_barrier(0);
-    if (g + 1 < ng) compute(b1, 1);
+    if (g + 1 < g1) compute(b1, 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  }
+
+  if constexpr (KS == 2) {
+    // the second half's sums through LDS (its buffers are free now): float4 i of lane l
+    // of column slot w at [i][w][l], so that consecutive lanes write consecutive 16 bytes
+    float4_t* red = reinterpret_cast<float4_t*>(smem_all);
+    if (half == 1) {
+#pragma unroll
+      for (int ms = 0; ms < WM; ++ms)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) red[((ms * WN + j) * 4 + wave) * 64 + lane] = acc[ms][j];
+    }
+    __syncthreads();
+    if (half == 1) return;
+#pragma unroll
+    for (int ms = 0; ms < WM; ++ms) {
+#pragma unroll
+      for (int j = 0; j < WN; ++j) acc[ms][j] += red[((ms * WN + j) * 4 + wave) * 64 + lane];
+      __builtin_amdgcn_sched_barrier(0);  // one row tile at a time: no reloads held live
+    }
   }
 
 #pragma unroll
@@ -209,13 +242,13 @@ __global__ void __launch_bounds__(kThreads) gemm_wide_kernel(WideArgs a) {
   }
 }
 
-template <int WN, bool ASYM>
+template <int WN, int KS, bool ASYM>
 hipError_t launch_wide_fmt(WideArgs a, hipStream_t st) {
   constexpr int BN = 4 * WN * 16;
-  const size_t lds = 2ull * kTileBytes;
+  const size_t lds = 2ull * KS * kTileBytes;
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_wide_kernel<WN, ASYM>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_wide_kernel<WN, KS, ASYM>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              static_cast<int>(lds));
     if (e != hipSuccess) return e;
@@ -224,8 +257,30 @@ hipError_t launch_wide_fmt(WideArgs a, hipStream_t st) {
   a.n_blocks_m = (a.M + kBM - 1) / kBM;
   a.n_blocks_n = (a.N + BN - 1) / BN;
   const unsigned blocks = static_cast<unsigned>(a.n_blocks_m) * static_cast<unsigned>(a.n_blocks_n);
-  hipLaunchKernelGGL((gemm_wide_kernel<WN, ASYM>), dim3(blocks), dim3(kThreads), lds, st, a);
+  hipLaunchKernelGGL((gemm_wide_kernel<WN, KS, ASYM>), dim3(blocks), dim3(256 * KS), lds, st, a);
   return hipGetLastError();
+}
+
+template <int WN, int KS>
+hipError_t launch_wide(const WideArgs& a, hipStream_t st) {
+  return a.zeros_off >= 0 ? launch_wide_fmt<WN, KS, true>(a, st) : launch_wide_fmt<WN, KS, false>(a, st);
+}
+
+// Column tiles per wavefront and K split for an M x N product, aiming at two workgroups
+// per CU (from sweeps on MI355X): 128 x 256 workgroup tiles when they give that many;
+// else 128 x 192 tiles when N divides into them and they do; else, with at most one
+// 128 x 256 block per CU, K split in two inside the workgroup.
+void pick_wide(int64_t M, int64_t N, int& wn, int& ks) {
+  const int64_t mb = (M + kBM - 1) / kBM;
+  const int64_t blocks4 = mb * ((N + 255) / 256), blocks3 = mb * ((N + 191) / 192);
+  wn = 4;
+  ks = 1;
+  if (blocks4 >= 512) return;
+  if (N % 192 == 0 && blocks3 >= 512) {
+    wn = 3;
+    return;
+  }
+  if (blocks4 <= 256) ks = 2;
 }
 
 }  // namespace
@@ -235,11 +290,10 @@ size_t gemm_wide_workspace_bytes(int64_t M, int64_t K) {
 }
 
 // X' into the workspace when inv_s_c is given (ws must hold M * K binary16), then the
-// product; wn selects 4 (128 x 256 workgroup tiles) or 2 (128 x 128) column tiles per
-// wavefront.
+// product. cfg = 10 * column tiles per wavefront + K split, or 0 for the default choice.
 hipError_t launch_gemm_wide(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
                             int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y,
-                            void* ws, int wn, hipStream_t st) {
+                            void* ws, int cfg, hipStream_t st) {
   const PackedLayout L = make_layout(N, K, kGroup, fmt);
   const uint16_t* xs = x;
   if (inv_s_c != nullptr) {
@@ -261,9 +315,15 @@ hipError_t launch_gemm_wide(const uint16_t* x, const uint16_t* inv_s_c, const vo
   a.K = static_cast<int>(K);
   a.n_groups = static_cast<int>(L.n_groups);
   a.n_tiles = static_cast<int>(L.n_tiles);
-  const bool asym = L.zeros_off >= 0;
-  if (wn == 4) return asym ? launch_wide_fmt<4, true>(a, st) : launch_wide_fmt<4, false>(a, st);
-  return asym ? launch_wide_fmt<2, true>(a, st) : launch_wide_fmt<2, false>(a, st);
+  int wn = cfg / 10, ks = cfg % 10;
+  if (cfg == 0) pick_wide(M, N, wn, ks);
+  if (wn == 4 && ks == 1) return launch_wide<4, 1>(a, st);
+  if (wn == 4 && ks == 2) return launch_wide<4, 2>(a, st);
+  if (wn == 3 && ks == 1) return launch_wide<3, 1>(a, st);
+  if (wn == 3 && ks == 2) return launch_wide<3, 2>(a, st);
+  if (wn == 2 && ks == 1) return launch_wide<2, 1>(a, st);
+  if (wn == 2 && ks == 2) return launch_wide<2, 2>(a, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace awq
