@@ -19,6 +19,7 @@ Also reported (same JSON line):
   batched           M = 8, 16, 32, 64 rows at 4096 -> 11008 (the GEMV -> matrix-core
                     crossover);
   llama70b_m1       8192 -> 28672 and 28672 -> 8192 at M = 1, asymmetric and symmetric;
+  scale_search      the AWQ exponent grid search (21 candidates) on one 4096 -> 11008 layer;
   gemm              the prefill GEMM at M = 2048 on the Llama-3-8B shapes (4096 -> 6144,
                     4096 -> 28672, 14336 -> 4096);
   unfused           awq_dequant to binary16 + the library fp16 GEMM (hipBLASLt through
@@ -271,6 +272,28 @@ def main():
                 del cp, L
                 torch.cuda.empty_cache()
         extra["llama70b_m1"] = rows70
+
+        # -------------------------------------- AWQ exponent search (NEXT-1), one 7B layer
+        log("AWQ scale search")
+        d = synth.layer_inputs(1, 1, 11008, 4096, layer=4)
+        w = torch.from_numpy(d["w"]).to(dev)
+        xc = torch.from_numpy(d["x_cal"]).to(dev)
+        sws = torch.empty(awq.awq_scale_search_workspace_bytes(xc.shape[0], 11008, 4096),
+                          dtype=torch.uint8, device=dev)
+        awq.awq_scale_search(w, xc, GROUP, awq.FMT_ASYM, 20, ws=sws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        best, losses = awq.awq_scale_search(w, xc, GROUP, awq.FMT_ASYM, 20, ws=sws)
+        e1.record()
+        torch.cuda.synchronize()
+        lo = losses.cpu().tolist()
+        extra["scale_search"] = {"layer": "4096->11008", "calibration_rows": int(xc.shape[0]),
+                                 "grid": 20, "ms": round(e0.elapsed_time(e1), 3),
+                                 "best_alpha": best.item(),
+                                 "loss_alpha0": round(lo[0], 4), "loss_best": round(min(lo), 4)}
+        del w, xc, sws
+        torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ prefill GEMM
     gemm = unfused = None

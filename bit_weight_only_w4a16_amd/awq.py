@@ -41,6 +41,9 @@ _SIGNATURES = {
     "awq_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "awq_gemv": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _sz, _vp]),
     "awq_gemm": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "awq_scale_search_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32]),
+    "awq_scale_search": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp, _vp,
+                                        _vp, _sz, _vp]),
 }
 EXPORTS = tuple(_SIGNATURES)
 
@@ -193,6 +196,31 @@ def awq_gemm(x, inv_s_c, packed, n: int, k: int, group: int = GROUP, fmt: int = 
              y=None, ws=None) -> torch.Tensor:
     """Matrix-core product, any M >= 1."""
     return _product("awq_gemm", x, inv_s_c, packed, n, k, group, fmt, y, ws)
+
+
+def awq_scale_search_workspace_bytes(rows: int, n: int, k: int, group: int = GROUP,
+                                     fmt: int = FMT_ASYM) -> int:
+    return int(lib().awq_scale_search_workspace_bytes(rows, n, k, group, fmt))
+
+
+def awq_scale_search(w, x_cal, group: int = GROUP, fmt: int = FMT_ASYM, grid: int = 20,
+                     ws=None):
+    """AWQ exponent search on the device: (best_alpha [1] float64, losses [grid+1]
+    float64), both device tensors, valid once the current stream is synchronised."""
+    n, k = w.shape
+    rows = x_cal.shape[0]
+    if x_cal.dim() != 2 or x_cal.shape[1] != k:
+        raise ValueError("x_cal must be [rows, K] with the weights' K")
+    need = awq_scale_search_workspace_bytes(rows, n, k, group, fmt)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=w.device)
+    losses = torch.empty(grid + 1, dtype=torch.float64, device=w.device)
+    best = torch.empty(1, dtype=torch.float64, device=w.device)
+    _check(lib().awq_scale_search(_dev(w, "w", torch.float16), _dev(x_cal, "x_cal", torch.float16),
+                                  rows, n, k, group, fmt, grid, losses.data_ptr(),
+                                  best.data_ptr(), _dev(ws, "ws", torch.uint8), ws.numel(),
+                                  _stream(w.device)), "awq_scale_search")
+    return best, losses
 
 
 # --------------------------------------------------------------------- convenience

@@ -149,4 +149,28 @@ int awq_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* packed, int
   return hip_status(awq::launch_gemm(x, inv_s_c, packed, M, N, K, fmt, y, ws, ws_bytes, stream));
 }
 
+size_t awq_scale_search_workspace_bytes(int64_t rows, int64_t N, int64_t K, int32_t group,
+                                        int32_t fmt) {
+  if (rows < 1 || rows > 256 || check_shape(N, K, group, fmt) != AWQ_OK) return 0;
+  return awq::scale_search_workspace_bytes(rows, N, K, group, fmt);
+}
+
+int awq_scale_search(const uint16_t* w, const uint16_t* x_cal, int64_t rows, int64_t N,
+                     int64_t K, int32_t group, int32_t fmt, int32_t grid, double* losses,
+                     double* best_alpha, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_shape(N, K, group, fmt);
+  if (rc != AWQ_OK) return rc;
+  if (w == nullptr || x_cal == nullptr || losses == nullptr || best_alpha == nullptr ||
+      ws == nullptr)
+    return AWQ_ERR_INVALID_ARG;
+  if (rows < 1 || rows > 256 || grid < 1 || grid > 1000) return AWQ_ERR_INVALID_ARG;
+  if (!aligned16(w) || !aligned16(x_cal) || !aligned16(ws) ||
+      (reinterpret_cast<uintptr_t>(losses) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(best_alpha) & 7u) != 0)
+    return AWQ_ERR_MISALIGNED;
+  if (ws_bytes < awq::scale_search_workspace_bytes(rows, N, K, group, fmt)) return AWQ_ERR_WORKSPACE;
+  return hip_status(awq::launch_scale_search(w, x_cal, rows, N, K, group, fmt, grid, losses,
+                                             best_alpha, ws, stream));
+}
+
 }  // extern "C"

@@ -62,6 +62,11 @@ hipError_t launch_gemv(const uint16_t* x, const uint16_t* inv_s_c, const void* p
                        size_t ws_bytes, hipStream_t st);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 size_t gemm_wide_workspace_bytes(int64_t M, int64_t K);
+size_t scale_search_workspace_bytes(int64_t rows, int64_t N, int64_t K, int32_t group,
+                                    int32_t fmt);
+hipError_t launch_scale_search(const uint16_t* w, const uint16_t* x_cal, int64_t rows,
+                               int64_t N, int64_t K, int32_t group, int32_t fmt, int32_t grid,
+                               double* losses, double* best_alpha, void* ws, hipStream_t st);
 hipError_t launch_gemm_wide(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
                             int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y,
                             void* ws, int cfg, hipStream_t st);

@@ -203,6 +203,40 @@ int awq_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* packed, int
              int64_t N, int64_t K, int32_t group, int32_t fmt, uint16_t* y, void* ws,
              size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Workspace bytes awq_scale_search needs for (rows, N, K, group, fmt); 0 for arguments it
+ * would reject.
+ */
+size_t awq_scale_search_workspace_bytes(int64_t rows, int64_t N, int64_t K, int32_t group,
+                                        int32_t fmt);
+
+/*
+ * awq_scale_search - grid search of the AWQ channel-scale exponent ("Quantization
+ * Paradigms for Edge Inference: AWQ, GPTQ, and FP8 Matrix Cores", section 3, second
+ * equation: the scale minimises || W X - Q(W diag(s)) diag(s)^-1 X || on calibration
+ * data). The pages leave the search space open; it is s = (mean_r |x_cal[r][k]|)^alpha
+ * (as awq_channel_scale) for alpha = i / grid, i = 0 .. grid.
+ * For each alpha the candidate is built and applied with this library's own kernels,
+ * as it would be deployed (awq_channel_scale, awq_pack, awq_repack, awq_gemm on the
+ * calibration rows, binary16 output), and scored against X_cal . W^T formed once in
+ * float32 from the unquantized binary16 weights:
+ *   losses[i] = sqrt( sum_{r,n} (ref[r][n] - y_i[r][n])^2 ),  summed in float64 in a
+ *   fixed order (the same bits on every call);
+ *   best_alpha[0] = i / grid for the first i with the smallest loss.
+ * w       device, [N][K] binary16 (unquantized, unfolded weights).
+ * x_cal   device, [rows][K] binary16 calibration activations, 1 <= rows <= 256.
+ * losses  device, [grid + 1] float64, written.  best_alpha device, [1] float64, written.
+ * ws      device workspace of ws_bytes >= awq_scale_search_workspace_bytes() bytes
+ *         (overwritten; holds the candidate's quantized layer and products).
+ * 1 <= grid <= 1000. Asynchronous on `stream` like every device entry point: the
+ * results are valid after the caller synchronises the stream.
+ * Errors: INVALID_ARG, UNSUPPORTED (group, sizes), MISALIGNED (w, x_cal, ws not 16-byte
+ * or losses, best_alpha not 8-byte aligned), WORKSPACE, HIP.
+ */
+int awq_scale_search(const uint16_t* w, const uint16_t* x_cal, int64_t rows, int64_t N,
+                     int64_t K, int32_t group, int32_t fmt, int32_t grid, double* losses,
+                     double* best_alpha, void* ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(awq.EXPORTS) == names
@@ -145,3 +145,24 @@ def test_ctypes_signature_matches_header():
         params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
         assert len(params) == len(argtypes), name
     _ = ctypes
+
+
+def test_scale_search_validation(lib):
+    need = lib.awq_scale_search_workspace_bytes(32, 256, 1024, 128, 0)
+    assert need > 256 * 1024 // 2                                   # holds a quantized layer
+    assert lib.awq_scale_search_workspace_bytes(0, 256, 1024, 128, 0) == 0
+    assert lib.awq_scale_search_workspace_bytes(257, 256, 1024, 128, 0) == 0
+    args = [P, P, 32, 256, 1024, 128, 0, 20, P, P, P, need, None]
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.awq_scale_search(*a)
+    assert call(a0=None) == INVALID                   # w NULL
+    assert call(a2=0) == INVALID                      # rows
+    assert call(a2=257) == INVALID
+    assert call(a7=0) == INVALID                      # grid
+    assert call(a5=64) == UNSUPPORTED                 # group
+    assert call(a8=P + 4) == MISALIGNED               # losses
+    assert call(a1=P + 2) == MISALIGNED               # x_cal
+    assert call(a11=need - 1) == WORKSPACE
