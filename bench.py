@@ -19,6 +19,7 @@ Also reported (same JSON line):
   batched           M = 8, 16, 32, 64 rows at 4096 -> 11008 (the GEMV -> matrix-core
                     crossover);
   llama70b_m1       8192 -> 28672 and 28672 -> 8192 at M = 1, asymmetric and symmetric;
+  group_sizes       the 4096 -> 11008 decode layer with groups of 32, 64, 128 and 4096;
   scale_search      the AWQ exponent grid search (21 candidates) on one 4096 -> 11008 layer;
   gemm              the prefill GEMM at M = 2048 on the Llama-3-8B shapes (4096 -> 6144,
                     4096 -> 28672, 14336 -> 4096);
@@ -272,6 +273,31 @@ def main():
                 del cp, L
                 torch.cuda.empty_cache()
         extra["llama70b_m1"] = rows70
+
+        # -------------------------------------- group sizes (NEXT-4): 4096 -> 11008, M = 1
+        log("group sizes")
+        gs_rows = []
+        for gsz in (32, 64, 128, 4096):
+            d = synth.layer_inputs(1, 1, 11008, 4096, layer=4)
+            w = torch.from_numpy(d["w"]).to(dev)
+            s_c, inv = awq.awq_channel_scale(torch.from_numpy(d["x_cal"]).to(dev), 0.5)
+            qw, sc, qz = awq.awq_pack(w, s_c, gsz, awq.FMT_ASYM)
+            pk = awq.awq_repack(qw, sc, qz, 11008, 4096, gsz, awq.FMT_ASYM)
+            del w, qw, sc, qz
+            L = {"n": 11008, "k": 4096, "fmt": awq.FMT_ASYM, "inv": inv,
+                 "x": torch.from_numpy(d["x"]).to(dev),
+                 "y": torch.empty((1, 11008), dtype=torch.float16, device=dev)}
+            rg = rotation(pk.numel())
+            cp = [pk] + [pk.clone() for _ in range(rg - 1)]
+            fn = lambda r, cp=cp, L=L, gsz=gsz: awq.awq_gemv(L["x"], L["inv"], cp[r], 11008, 4096,
+                                                          gsz, awq.FMT_ASYM, y=L["y"])
+            us = graph_us([lambda r=r: fn(r) for r in range(rg)], 10)
+            byts = rl.algorithmic_bytes(1, 11008, 4096, gsz, rl.FMT_ASYM, True)
+            gs_rows.append({"group": gsz, "us": round(us, 3), "GB/s": round(byts / us / 1e3, 1),
+                            "algorithmic_bytes": byts})
+            del cp, pk
+            torch.cuda.empty_cache()
+        extra["group_sizes"] = {"shape": "4096->11008", "M": 1, "rows": gs_rows}
 
         # -------------------------------------- AWQ exponent search (NEXT-1), one 7B layer
         log("AWQ scale search")

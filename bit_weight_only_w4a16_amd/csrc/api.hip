@@ -17,7 +17,10 @@ int check_shape(int64_t N, int64_t K, int32_t group, int32_t fmt) {
   if (N <= 0 || K <= 0 || group <= 0) return AWQ_ERR_INVALID_ARG;
   if (fmt != AWQ_FMT_ASYM && fmt != AWQ_FMT_SYM8) return AWQ_ERR_INVALID_ARG;
   if (N % 8 != 0 || K % 8 != 0 || K % group != 0) return AWQ_ERR_INVALID_ARG;
-  if (group != kGroup) return AWQ_ERR_UNSUPPORTED;
+  // groups of 32 or 64 channels, or any multiple of 128 that divides K (per-channel
+  // included: group == K); K itself a multiple of 128 (the unit width)
+  if (K % kGroup != 0) return AWQ_ERR_UNSUPPORTED;
+  if (group != 32 && group != 64 && group % kGroup != 0) return AWQ_ERR_UNSUPPORTED;
   if (N * K >= (int64_t{1} << 31) || N >= (int64_t{1} << 30) || K > (int64_t{1} << 22))
     return AWQ_ERR_UNSUPPORTED;
   return AWQ_OK;
@@ -137,7 +140,7 @@ int awq_gemv(const uint16_t* x, const uint16_t* inv_s_c, const void* packed, int
   if (rc != AWQ_OK) return rc;
   if (M > 16) return AWQ_ERR_UNSUPPORTED;
   if (M == 0) return AWQ_OK;
-  return hip_status(awq::launch_gemv(x, inv_s_c, packed, M, N, K, fmt, y, ws, ws_bytes, stream));
+  return hip_status(awq::launch_gemv(x, inv_s_c, packed, M, N, K, group, fmt, y, ws, ws_bytes, stream));
 }
 
 int awq_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* packed, int64_t M,
@@ -146,7 +149,7 @@ int awq_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* packed, int
   int rc = check_product(x, inv_s_c, packed, M, N, K, group, fmt, y, ws, ws_bytes);
   if (rc != AWQ_OK) return rc;
   if (M == 0) return AWQ_OK;
-  return hip_status(awq::launch_gemm(x, inv_s_c, packed, M, N, K, fmt, y, ws, ws_bytes, stream));
+  return hip_status(awq::launch_gemm(x, inv_s_c, packed, M, N, K, group, fmt, y, ws, ws_bytes, stream));
 }
 
 size_t awq_scale_search_workspace_bytes(int64_t rows, int64_t N, int64_t K, int32_t group,

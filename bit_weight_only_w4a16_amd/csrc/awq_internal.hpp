@@ -7,17 +7,21 @@
 namespace awq {
 
 // ---------------------------------------------------------------- layout constants
-// gfx950 packed layout, version 2: a 1 KiB unit holds 16 output rows x one group of 128
-// input channels. Lane l of a wavefront owns 16 bytes of a unit: row l % 16, channels
-// 32 (l / 16) + 0..31 of the group, as four 32-bit words of eight channels each.
+// gfx950 packed layout, version 3: a 1 KiB unit holds 16 output rows x 128 input
+// channels. Lane l of a wavefront owns 16 bytes of a unit: row l % 16, channels
+// 32 (l / 16) + 0..31 of the unit, as four 32-bit words of eight channels each. Each
+// unit carries S = max(1, 128 / G) sets of 16 scales (and zeros) for group size G: with
+// G = 32 or 64 one set per group inside the unit (lane l uses set (l / 16) * S / 4),
+// with G a multiple of 128 (per-channel included) the set of the group the unit lies in.
 constexpr int kTileN = 16;        // output rows per unit
-constexpr int kGroup = 128;       // input channels per unit (the group size)
+constexpr int kGroup = 128;       // input channels per unit
 constexpr int kUnitBytes = 1024;  // 16 rows x 128 channels x 4 bits
-constexpr int kLayoutVersion = 2;
+constexpr int kLayoutVersion = 3;
 
 struct PackedLayout {
   int64_t n_tiles;       // ceil(N / 16)
-  int64_t n_groups;      // K / 128
+  int64_t n_groups;      // units along K: K / 128
+  int64_t sets;          // scale / zero sets per unit: max(1, 128 / group)
   int64_t codes_off;     // byte offsets inside the packed buffer
   int64_t scales_off;
   int64_t zeros_off;     // -1 for the symmetric format
@@ -27,19 +31,23 @@ struct PackedLayout {
 inline PackedLayout make_layout(int64_t N, int64_t K, int32_t group, int32_t fmt) {
   PackedLayout L;
   L.n_tiles = (N + kTileN - 1) / kTileN;
-  L.n_groups = K / group;
+  L.n_groups = K / kGroup;
+  L.sets = group < kGroup ? kGroup / group : 1;
   L.codes_off = 0;
   L.scales_off = L.n_tiles * L.n_groups * kUnitBytes;
-  int64_t end = L.scales_off + L.n_tiles * L.n_groups * kTileN * 2;
+  int64_t end = L.scales_off + L.n_tiles * L.n_groups * L.sets * kTileN * 2;
   if (fmt == 0) {
     L.zeros_off = (end + 255) / 256 * 256;
-    end = L.zeros_off + L.n_tiles * L.n_groups * (kTileN / 2);
+    end = L.zeros_off + L.n_tiles * L.n_groups * L.sets * (kTileN / 2);
   } else {
     L.zeros_off = -1;
   }
   L.total_bytes = (end + 255) / 256 * 256;
   return L;
 }
+
+// the scale / zero set lane (r, p) of a unit uses: p * S / 4 for S sets per unit
+__host__ __device__ inline int lane_set(int p, int sets) { return (p * sets) >> 2; }
 
 // ------------------------------------------------------------ launchers (per file)
 hipError_t launch_channel_scale(const uint16_t* x_cal, int64_t rows, int64_t K, double alpha,
@@ -58,8 +66,8 @@ hipError_t launch_dequant_packed(const void* packed, int64_t N, int64_t K, int32
 
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
-                       int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y, void* ws,
-                       size_t ws_bytes, hipStream_t st);
+                       int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt, uint16_t* y,
+                       void* ws, size_t ws_bytes, hipStream_t st);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 size_t gemm_wide_workspace_bytes(int64_t M, int64_t K);
 size_t scale_search_workspace_bytes(int64_t rows, int64_t N, int64_t K, int32_t group,
@@ -68,11 +76,11 @@ hipError_t launch_scale_search(const uint16_t* w, const uint16_t* x_cal, int64_t
                                int64_t N, int64_t K, int32_t group, int32_t fmt, int32_t grid,
                                double* losses, double* best_alpha, void* ws, hipStream_t st);
 hipError_t launch_gemm_wide(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
-                            int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y,
-                            void* ws, int cfg, hipStream_t st);
+                            int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt,
+                            uint16_t* y, void* ws, int cfg, hipStream_t st);
 hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
-                       int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y, void* ws,
-                       size_t ws_bytes, hipStream_t st);
+                       int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt, uint16_t* y,
+                       void* ws, size_t ws_bytes, hipStream_t st);
 
 // ------------------------------------------------------------------ device helpers
 // Buffer resource over [base, base + bytes): loads take a wavefront-uniform SGPR offset

@@ -48,7 +48,7 @@ struct GemmArgs {
   int64_t zeros_off;
   uint32_t packed_bytes;
   float* part;  // split-K partial sums [splits][M][N], or NULL (one split)
-  int M, N, K, n_groups, n_tiles, n_blocks_n, n_blocks_m, splits;
+  int M, N, K, n_groups, n_tiles, n_blocks_n, n_blocks_m, splits, sets;
 };
 
 // SCHED > 0: ask the scheduler to issue each matrix instruction followed by SCHED VALU
@@ -84,15 +84,18 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
   // addressed by wavefront-uniform (SGPR) offsets (tiles past the last one are clamped:
   // their rows are >= N and never stored). Few SGPRs: no resource ends up in VGPRs.
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.packed, a.packed_bytes);
+  const uint32_t sbytes = 2 * kTileN * a.sets, zbytes = 8 * a.sets;  // per unit
   uint32_t code_off[WN], scale_off[WN], zero_off[WN];
 #pragma unroll
   for (int j = 0; j < WN; ++j) {
     const uint32_t tile = static_cast<uint32_t>(min(n_blk / kTileN + wn * WN + j, a.n_tiles - 1));
     code_off[j] = tile * ng * kUnitBytes;
-    scale_off[j] = static_cast<uint32_t>(a.scales_off) + tile * ng * (2 * kTileN);
-    zero_off[j] = ASYM ? static_cast<uint32_t>(a.zeros_off) + tile * ng * 8 : 0u;
+    scale_off[j] = static_cast<uint32_t>(a.scales_off) + tile * ng * sbytes;
+    zero_off[j] = ASYM ? static_cast<uint32_t>(a.zeros_off) + tile * ng * zbytes : 0u;
   }
-  const uint32_t lane_code = 16u * lane, lane_scale = 2u * r, lane_zero = 4u * (r >> 3);
+  const int lset = lane_set(p, a.sets);
+  const uint32_t lane_code = 16u * lane, lane_scale = 2u * (kTileN * lset + r),
+                 lane_zero = 4u * (2 * lset + (r >> 3));
   const int zshift = 4 * (r & 7);
 
   // X' rows of this block as one buffer resource (rows past M read as 0), and inv_s_c
@@ -146,8 +149,8 @@ __global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
       b.c[j] = buf_load16(rp, lane_code + skip, code_off[j] + gg * kUnitBytes);
-      b.s[j] = buf_load2(rp, lane_scale + skip, scale_off[j] + gg * (2 * kTileN));
-      if (ASYM) b.z[j] = buf_load4(rp, lane_zero + skip, zero_off[j] + gg * 8);
+      b.s[j] = buf_load2(rp, lane_scale + skip, scale_off[j] + gg * sbytes);
+      if (ASYM) b.z[j] = buf_load4(rp, lane_zero + skip, zero_off[j] + gg * zbytes);
     }
   };
 
@@ -335,8 +338,8 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
-                       int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y, void* ws,
-                       size_t ws_bytes, hipStream_t st) {
+                       int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt, uint16_t* y,
+                       void* ws, size_t ws_bytes, hipStream_t st) {
   // large M: wide wavefront tiles, X' from the workspace (or pre-scaled by the caller);
   // AWQ_GEMM_WIDE = "0" keeps the narrow kernel, "<column tiles><K split>" (41, 42, 31,
   // 32, 21, 22) forces a wide configuration (for tuning sweeps)
@@ -344,9 +347,9 @@ hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* p
   const bool wide_ok = inv_s_c == nullptr || (ws != nullptr && ws_bytes >= gemm_wide_workspace_bytes(M, K));
   if (M >= kWideMinM && wide_ok && !(wide && wide[0] == '0')) {
     const int cfg = wide ? atoi(wide) : 0;
-    return launch_gemm_wide(x, inv_s_c, packed, M, N, K, fmt, y, ws, cfg, st);
+    return launch_gemm_wide(x, inv_s_c, packed, M, N, K, group, fmt, y, ws, cfg, st);
   }
-  const PackedLayout L = make_layout(N, K, kGroup, fmt);
+  const PackedLayout L = make_layout(N, K, group, fmt);
   GemmArgs a;
   a.x = x;
   a.inv = inv_s_c;
@@ -360,6 +363,7 @@ hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* p
   a.K = static_cast<int>(K);
   a.n_groups = static_cast<int>(L.n_groups);
   a.n_tiles = static_cast<int>(L.n_tiles);
+  a.sets = static_cast<int>(L.sets);
   // split K when the output blocks alone leave CUs idle and the caller gave a workspace
   // for the partial sums (without one the product runs unsplit)
   a.splits = 1;

@@ -42,7 +42,7 @@ struct WideArgs {
   int64_t scales_off;
   int64_t zeros_off;
   uint32_t packed_bytes;
-  int M, N, K, n_groups, n_tiles, n_blocks_m, n_blocks_n;
+  int M, N, K, n_groups, n_tiles, n_blocks_m, n_blocks_n, sets;
 };
 
 __global__ void __launch_bounds__(256) prescale_kernel(const uint16_t* x, const uint16_t* inv,
@@ -85,15 +85,18 @@ __global__ void __launch_bounds__(256 * KS) gemm_wide_kernel(WideArgs a) {
   // weights: one resource over the packed layer, per-tile SGPR offsets (tiles past the
   // last are clamped: their outputs are never stored)
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.packed, a.packed_bytes);
+  const uint32_t sbytes = 2 * kTileN * a.sets, zbytes = 8 * a.sets;  // per unit
   uint32_t code_off[WN], scale_off[WN], zero_off[WN];
 #pragma unroll
   for (int j = 0; j < WN; ++j) {
     const uint32_t tile = static_cast<uint32_t>(min(n_blk / kTileN + wave * WN + j, a.n_tiles - 1));
     code_off[j] = tile * ng * kUnitBytes;
-    scale_off[j] = static_cast<uint32_t>(a.scales_off) + tile * ng * (2 * kTileN);
-    zero_off[j] = ASYM ? static_cast<uint32_t>(a.zeros_off) + tile * ng * 8 : 0u;
+    scale_off[j] = static_cast<uint32_t>(a.scales_off) + tile * ng * sbytes;
+    zero_off[j] = ASYM ? static_cast<uint32_t>(a.zeros_off) + tile * ng * zbytes : 0u;
   }
-  const uint32_t lane_code = 16u * lane, lane_scale = 2u * r, lane_zero = 4u * (r >> 3);
+  const int lset = lane_set(p, a.sets);
+  const uint32_t lane_code = 16u * lane, lane_scale = 2u * (kTileN * lset + r),
+                 lane_zero = 4u * (2 * lset + (r >> 3));
   const int zshift = 4 * (r & 7);
 
   // activations: this block's rows (rows past M read as 0). Wavefront w fills LDS rows
@@ -134,8 +137,8 @@ __global__ void __launch_bounds__(256 * KS) gemm_wide_kernel(WideArgs a) {
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
       b.c[j] = buf_load16(rp, lane_code + skip, code_off[j] + gg * kUnitBytes);
-      b.s[j] = buf_load2(rp, lane_scale + skip, scale_off[j] + gg * (2 * kTileN));
-      if (ASYM) b.z[j] = buf_load4(rp, lane_zero + skip, zero_off[j] + gg * 8);
+      b.s[j] = buf_load2(rp, lane_scale + skip, scale_off[j] + gg * sbytes);
+      if (ASYM) b.z[j] = buf_load4(rp, lane_zero + skip, zero_off[j] + gg * zbytes);
     }
   };
 
@@ -292,9 +295,9 @@ size_t gemm_wide_workspace_bytes(int64_t M, int64_t K) {
 // X' into the workspace when inv_s_c is given (ws must hold M * K binary16), then the
 // product. cfg = 10 * column tiles per wavefront + K split, or 0 for the default choice.
 hipError_t launch_gemm_wide(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
-                            int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y,
-                            void* ws, int cfg, hipStream_t st) {
-  const PackedLayout L = make_layout(N, K, kGroup, fmt);
+                            int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt,
+                            uint16_t* y, void* ws, int cfg, hipStream_t st) {
+  const PackedLayout L = make_layout(N, K, group, fmt);
   const uint16_t* xs = x;
   if (inv_s_c != nullptr) {
     uint16_t* dst = static_cast<uint16_t*>(ws);
@@ -315,6 +318,7 @@ hipError_t launch_gemm_wide(const uint16_t* x, const uint16_t* inv_s_c, const vo
   a.K = static_cast<int>(K);
   a.n_groups = static_cast<int>(L.n_groups);
   a.n_tiles = static_cast<int>(L.n_tiles);
+  a.sets = static_cast<int>(L.sets);
   int wn = cfg / 10, ks = cfg % 10;
   if (cfg == 0) pick_wide(M, N, wn, ks);
   if (wn == 4 && ks == 1) return launch_wide<4, 1>(a, st);

@@ -51,7 +51,7 @@ struct MvArgs {
   uint16_t* y;
   int64_t scales_off;
   int64_t zeros_off;
-  int N, K, n_groups, phase_groups;
+  int N, K, n_groups, phase_groups, sets;
 };
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -62,7 +62,10 @@ struct XPass {
   uint4 inv;
 };
 
-template <int M, int WAVES, int BATCH, bool ASYM>
+// EXACT (groups of 32 or 64 channels, several scale sets per unit): the weights are
+// dequantized exactly to W_d before the matrix core, which then sums across groups; the
+// per-group correction needs one scale per matrix-core sum and does not apply.
+template <int M, int WAVES, int BATCH, bool ASYM, bool EXACT>
 __global__ void __launch_bounds__(WAVES * 64) gemv_kernel(MvArgs a) {
   constexpr int JM = M < 4 ? M : 4;  // D rows per lane that can be real rows
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -82,11 +85,15 @@ __global__ void __launch_bounds__(WAVES * 64) gemv_kernel(MvArgs a) {
 
   const __amdgpu_buffer_rsrc_t rcodes =
       make_rsrc(a.packed + static_cast<int64_t>(t) * ng * kUnitBytes, ng * kUnitBytes);
+  const int sets = a.sets;
+  const uint32_t sbytes = 2 * kTileN * sets, zbytes = 8 * sets;  // per unit
   const __amdgpu_buffer_rsrc_t rscales =
-      make_rsrc(a.packed + a.scales_off + static_cast<int64_t>(t) * ng * (2 * kTileN), ng * 2 * kTileN);
+      make_rsrc(a.packed + a.scales_off + static_cast<int64_t>(t) * ng * sbytes, ng * sbytes);
   const __amdgpu_buffer_rsrc_t rzeros =
-      make_rsrc(a.packed + (ASYM ? a.zeros_off : 0) + static_cast<int64_t>(t) * ng * 8, ng * 8);
-  const uint32_t lane_code = 16u * lane, lane_scale = 2u * r, lane_zero = 4u * (r >> 3);
+      make_rsrc(a.packed + (ASYM ? a.zeros_off : 0) + static_cast<int64_t>(t) * ng * zbytes, ng * zbytes);
+  const int lset = lane_set(p, sets);
+  const uint32_t lane_code = 16u * lane, lane_scale = 2u * (kTileN * lset + r),
+                 lane_zero = 4u * (2 * lset + (r >> 3));
   const int zshift = 4 * (r & 7);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, static_cast<uint32_t>(M * a.K * 2));
   const __amdgpu_buffer_rsrc_t rinv =
@@ -97,6 +104,7 @@ __global__ void __launch_bounds__(WAVES * 64) gemv_kernel(MvArgs a) {
   float yacc[JM];
 #pragma unroll
   for (int j = 0; j < JM; ++j) yacc[j] = 0.0f;
+  float4_t dacc = {0.0f, 0.0f, 0.0f, 0.0f};  // EXACT: sum over groups of X' W_d
 
   struct Batch {
     uint4 c[BATCH];
@@ -110,8 +118,8 @@ __global__ void __launch_bounds__(WAVES * 64) gemv_kernel(MvArgs a) {
       const uint32_t g = live ? static_cast<uint32_t>(ph0 + wave + WAVES * (jb + u)) : 0u;
       const uint32_t skip = live ? 0u : kNoLoad;
       b.c[u] = buf_load16(rcodes, lane_code + skip, g * kUnitBytes);
-      b.s[u] = buf_load2(rscales, lane_scale + skip, g * (2 * kTileN));
-      if (ASYM) b.z[u] = buf_load4(rzeros, lane_zero + skip, g * 8);
+      b.s[u] = buf_load2(rscales, lane_scale + skip, g * sbytes);
+      if (ASYM) b.z[u] = buf_load4(rzeros, lane_zero + skip, g * zbytes);
     }
   };
   auto compute = [&](const Batch& b, int jb, int nj) {
@@ -121,6 +129,20 @@ __global__ void __launch_bounds__(WAVES * 64) gemv_kernel(MvArgs a) {
         const int gl = wave + WAVES * (jb + u);
         const _Float16* xg = xs + arow * PK + gl * kGroup + 32 * p;
         const uint32_t words[4] = {b.c[u].x, b.c[u].y, b.c[u].z, b.c[u].w};
+        if constexpr (EXACT) {
+          const uint32_t z = ASYM ? (b.z[u] >> zshift) & 0xFu : 8u;
+          const half2_t s2 = as_h2(b.s[u] | (b.s[u] << 16));
+          const uint32_t nz1024 = neg_off1024(z), nz64 = neg_off64(z);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            half2_t dq[4];
+            dequant_word(words[i], nz1024, nz64, s2, dq);
+            const half8_t bf = {dq[0].x, dq[0].y, dq[1].x, dq[1].y, dq[2].x, dq[2].y, dq[3].x, dq[3].y};
+            const half8_t af = *reinterpret_cast<const half8_t*>(xg + 8 * i);
+            dacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, dacc, 0, 0, 0);
+          }
+          continue;
+        }
         float4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -213,6 +235,10 @@ __global__ void __launch_bounds__(WAVES * 64) gemv_kernel(MvArgs a) {
     }
   }
 
+  if constexpr (EXACT) {
+#pragma unroll
+    for (int j = 0; j < JM; ++j) yacc[j] = dacc[j];
+  }
   // the wavefronts' partial sums through LDS; one thread per (row, output) writes y
 #pragma unroll
   for (int j = 0; j < JM; ++j) {
@@ -244,26 +270,31 @@ size_t smem_bytes(int M, int phase_groups, int waves) {
          4ull * waves * M * kTileN;
 }
 
-template <int M, int WAVES, int BATCH, bool ASYM>
+template <int M, int WAVES, int BATCH, bool ASYM, bool EXACT>
 hipError_t launch_fmt(const MvArgs& a, int64_t n_tiles, hipStream_t st) {
   const size_t lds = smem_bytes(M, a.phase_groups, WAVES);
   static bool attr_set = false;  // benign race: every thread sets the same value
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemv_kernel<M, WAVES, BATCH, ASYM>),
+        reinterpret_cast<const void*>(&gemv_kernel<M, WAVES, BATCH, ASYM, EXACT>),
         hipFuncAttributeMaxDynamicSharedMemorySize, kLdsAlone + 4 * WAVES * M * kTileN);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemv_kernel<M, WAVES, BATCH, ASYM>), dim3(static_cast<unsigned>(n_tiles)),
+  hipLaunchKernelGGL((gemv_kernel<M, WAVES, BATCH, ASYM, EXACT>), dim3(static_cast<unsigned>(n_tiles)),
                      dim3(WAVES * 64), lds, st, a);
   return hipGetLastError();
 }
 
 template <int M, int WAVES, int BATCH>
 hipError_t launch_cfg(const MvArgs& a, int64_t n_tiles, hipStream_t st) {
-  if (a.zeros_off >= 0) return launch_fmt<M, WAVES, BATCH, true>(a, n_tiles, st);
-  return launch_fmt<M, WAVES, BATCH, false>(a, n_tiles, st);
+  const bool asym = a.zeros_off >= 0;
+  if (a.sets > 1) {
+    return asym ? launch_fmt<M, WAVES, BATCH, true, true>(a, n_tiles, st)
+                : launch_fmt<M, WAVES, BATCH, false, true>(a, n_tiles, st);
+  }
+  return asym ? launch_fmt<M, WAVES, BATCH, true, false>(a, n_tiles, st)
+              : launch_fmt<M, WAVES, BATCH, false, false>(a, n_tiles, st);
 }
 
 // From sweeps on MI355X (4096 <= K, N <= 28672): long rows on few tiles (K >= 8192,
@@ -296,9 +327,9 @@ hipError_t launch_m1(const MvArgs& a, int64_t n_tiles, hipStream_t st) {
 size_t gemv_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
 
 hipError_t launch_gemv(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
-                       int64_t M, int64_t N, int64_t K, int32_t fmt, uint16_t* y, void*, size_t,
-                       hipStream_t st) {
-  const PackedLayout L = make_layout(N, K, kGroup, fmt);
+                       int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt, uint16_t* y,
+                       void*, size_t, hipStream_t st) {
+  const PackedLayout L = make_layout(N, K, group, fmt);
   MvArgs a;
   a.x = x;
   a.inv = inv_s_c;
@@ -309,6 +340,7 @@ hipError_t launch_gemv(const uint16_t* x, const uint16_t* inv_s_c, const void* p
   a.N = static_cast<int>(N);
   a.K = static_cast<int>(K);
   a.n_groups = static_cast<int>(L.n_groups);
+  a.sets = static_cast<int>(L.sets);
   a.phase_groups = phase_groups_for(static_cast<int>(M), a.n_groups, L.n_tiles);
   switch (M) {
     case 1: return launch_m1(a, L.n_tiles, st);

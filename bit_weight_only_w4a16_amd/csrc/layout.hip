@@ -2,8 +2,10 @@
 // dequantizers (one per layout) used as parity probes and as the unfused baseline.
 //
 // gfx950 layout (byte-level definition in awq.h): a 1 KiB unit holds 16 output rows x
-// one group of 128 input channels. Lane l of a wavefront owns the 16 bytes at 16 l: row
-// l % 16, channels 32 (l / 16) .. + 31 of the group, as four words of eight channels.
+// 128 input channels, with one scale (and zero) set per group inside it for groups of
+// 32 or 64 channels, or the set of its group for groups of 128 or more. Lane l of a
+// wavefront owns the 16 bytes at 16 l: row l % 16, channels 32 (l / 16) .. + 31 of the
+// unit, as four words of eight channels.
 // One wavefront load instruction therefore moves a whole unit, fully coalesced; for the
 // matrix cores the same 16 bytes are the B operands of four v_mfma_f32_16x16x32_f16
 // (word i feeds step i: lane l gives column l % 16 and k slots 8 (l / 16) .. + 7).
@@ -28,13 +30,15 @@ __device__ __forceinline__ uint32_t interleave_nibbles(uint32_t w) {
   return r;
 }
 
-// one thread per (tile t, group g, lane l): 16 bytes of codes, plus the lane's scale
-// (lanes 0..15) and the two zero words of the unit (lanes 0 and 8)
+// one thread per (tile t, unit g, lane l): 16 bytes of codes; lanes with p < S also
+// write row r's scale of set p (and, for r = 0 and 8, the set's two zero words). Set p
+// of unit g is canonical group g * 128 / G + p for G < 128, else g * 128 / G.
 __global__ void repack_kernel(const int32_t* __restrict__ qweight,
                               const uint16_t* __restrict__ scales,
                               const int32_t* __restrict__ qzeros, int N, int K, int n_groups,
-                              uint4* __restrict__ codes, uint16_t* __restrict__ pscales,
-                              uint32_t* __restrict__ pzeros, int64_t total) {
+                              int group, int sets, uint4* __restrict__ codes,
+                              uint16_t* __restrict__ pscales, uint32_t* __restrict__ pzeros,
+                              int64_t total) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= total) return;
   const int l = static_cast<int>(i & 63);
@@ -54,12 +58,14 @@ __global__ void repack_kernel(const int32_t* __restrict__ qweight,
     out.w = interleave_nibbles(in.w);
   }
   codes[i] = out;
-  if (p == 0) {
-    pscales[unit * kTileN + r] = n < N ? scales[static_cast<int64_t>(g) * N + n] : uint16_t{0};
+  if (p < sets) {
+    const int64_t cg = static_cast<int64_t>(g) * kGroup / group + (group < kGroup ? p : 0);
+    const int64_t set = unit * sets + p;
+    pscales[set * kTileN + r] = n < N ? scales[cg * N + n] : uint16_t{0};
     if (pzeros && (r & 7) == 0) {
-      // zeros of rows 16 t + r .. + 7: the canonical word (16 t + r) / 8 of group g
-      pzeros[unit * 2 + (r >> 3)] =
-          n < N ? static_cast<uint32_t>(qzeros[static_cast<int64_t>(g) * (N / 8) + n / 8]) : 0u;
+      // zeros of rows 16 t + r .. + 7: the canonical word (16 t + r) / 8 of group cg
+      pzeros[set * 2 + (r >> 3)] =
+          n < N ? static_cast<uint32_t>(qzeros[cg * (N / 8) + n / 8]) : 0u;
     }
   }
 }
@@ -97,8 +103,9 @@ __global__ void dequant_canonical_kernel(const int32_t* __restrict__ qweight,
 // gfx950 layout -> W_d, one thread per (tile, group, lane): 32 channels of one row,
 // through the same magic-number unpack the matrix-core kernel uses.
 __global__ void dequant_packed_kernel(const uint8_t* __restrict__ packed, int N, int K,
-                                      int n_groups, int64_t scales_off, int64_t zeros_off,
-                                      uint16_t* __restrict__ out, int64_t total) {
+                                      int n_groups, int sets, int64_t scales_off,
+                                      int64_t zeros_off, uint16_t* __restrict__ out,
+                                      int64_t total) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= total) return;
   const int l = static_cast<int>(i & 63);
@@ -108,10 +115,11 @@ __global__ void dequant_packed_kernel(const uint8_t* __restrict__ packed, int N,
   const int r = l & 15, p = l >> 4;
   const int64_t n = t * kTileN + r;
   if (n >= N) return;
-  const uint16_t sb = reinterpret_cast<const uint16_t*>(packed + scales_off)[unit * kTileN + r];
+  const int64_t set = unit * sets + lane_set(p, sets);
+  const uint16_t sb = reinterpret_cast<const uint16_t*>(packed + scales_off)[set * kTileN + r];
   uint32_t z = 8;
   if (zeros_off >= 0) {
-    const uint32_t zw = reinterpret_cast<const uint32_t*>(packed + zeros_off)[unit * 2 + (r >> 3)];
+    const uint32_t zw = reinterpret_cast<const uint32_t*>(packed + zeros_off)[set * 2 + (r >> 3)];
     z = (zw >> (4 * (r & 7))) & 0xFu;
   }
   const half2_t s2 = as_h2(static_cast<uint32_t>(sb) | (static_cast<uint32_t>(sb) << 16));
@@ -141,8 +149,8 @@ hipError_t launch_repack(const int32_t* qweight, const uint16_t* scales, const i
   const int64_t total = L.n_tiles * L.n_groups * 64;
   hipLaunchKernelGGL(repack_kernel, dim3(blocks_for(total, 256)), dim3(256), 0, st, qweight,
                      scales, fmt == 0 ? qzeros : nullptr, static_cast<int>(N),
-                     static_cast<int>(K), static_cast<int>(L.n_groups),
-                     reinterpret_cast<uint4*>(base + L.codes_off),
+                     static_cast<int>(K), static_cast<int>(L.n_groups), static_cast<int>(group),
+                     static_cast<int>(L.sets), reinterpret_cast<uint4*>(base + L.codes_off),
                      reinterpret_cast<uint16_t*>(base + L.scales_off),
                      fmt == 0 ? reinterpret_cast<uint32_t*>(base + L.zeros_off) : nullptr, total);
   return hipGetLastError();
@@ -165,8 +173,8 @@ hipError_t launch_dequant_packed(const void* packed, int64_t N, int64_t K, int32
   const int64_t total = L.n_tiles * L.n_groups * 64;
   hipLaunchKernelGGL(dequant_packed_kernel, dim3(blocks_for(total, 256)), dim3(256), 0, st,
                      static_cast<const uint8_t*>(packed), static_cast<int>(N),
-                     static_cast<int>(K), static_cast<int>(L.n_groups), L.scales_off,
-                     L.zeros_off, w_out, total);
+                     static_cast<int>(K), static_cast<int>(L.n_groups), static_cast<int>(L.sets),
+                     L.scales_off, L.zeros_off, w_out, total);
   return hipGetLastError();
 }
 

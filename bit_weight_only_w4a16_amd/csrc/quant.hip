@@ -57,37 +57,48 @@ __global__ void channel_scale_kernel(const uint16_t* __restrict__ x_cal, int row
   if (inv_s_c) inv_s_c[k] = f64_to_f16_rn(1.0 / f16_bits_to_f64(s));
 }
 
-// One workgroup quantizes 8 consecutive rows of one group: group/8 threads per row,
-// each owning 8 consecutive channels (one output word). Rows sit in contiguous lanes
-// so that the group min/max reduce within a wavefront.
-template <int GROUP>
-__global__ void __launch_bounds__(8 * (GROUP / 8))
-pack_kernel(const uint16_t* __restrict__ w, const uint16_t* __restrict__ s_c, int K, int fmt,
-            int32_t* __restrict__ qweight, uint16_t* __restrict__ scales,
+// One workgroup quantizes 8 consecutive rows of one group: TPR = min(group / 8, 16)
+// threads per row, each owning every TPR-th 8-channel vector (one output word each).
+// Rows sit in contiguous lanes so that the group min/max reduce within a wavefront.
+template <int TPR>
+__global__ void __launch_bounds__(8 * TPR)
+pack_kernel(const uint16_t* __restrict__ w, const uint16_t* __restrict__ s_c, int K, int group,
+            int fmt, int32_t* __restrict__ qweight, uint16_t* __restrict__ scales,
             int32_t* __restrict__ qzeros, int N) {
-  constexpr int TPR = GROUP / 8;  // threads per row
+  // a block quantizes one group of 8 rows; TPR threads per row, each taking the
+  // 8-channel vectors t, t + TPR, ... of the group (group / (8 TPR) of them)
   const int row_in_blk = threadIdx.x / TPR;
   const int t = threadIdx.x % TPR;
   const int n = blockIdx.x * 8 + row_in_blk;
   const int g = blockIdx.y;
-  const int k0 = g * GROUP + t * 8;
-  const int64_t base = static_cast<int64_t>(n) * K + k0;
+  const int nvec = group / (8 * TPR);
+  const int64_t row_base = static_cast<int64_t>(n) * K + static_cast<int64_t>(g) * group;
 
   // Fold: binary16 x binary16 is exact in float64; one rounding to binary16.
-  const uint4 wraw = *reinterpret_cast<const uint4*>(w + base);
-  uint4 sraw = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
-  if (s_c) sraw = *reinterpret_cast<const uint4*>(s_c + k0);
-  const uint32_t wv[4] = {wraw.x, wraw.y, wraw.z, wraw.w};
-  const uint32_t sv[4] = {sraw.x, sraw.y, sraw.z, sraw.w};
-  double v[8];
-  double vmin = 0.0, vmax = 0.0;
+  auto fold8 = [&](int j, double v[8]) {
+    const int k = g * group + (t + j * TPR) * 8;
+    const uint4 wraw = *reinterpret_cast<const uint4*>(w + row_base + (t + j * TPR) * 8);
+    uint4 sraw = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+    if (s_c) sraw = *reinterpret_cast<const uint4*>(s_c + k);
+    const uint32_t wv[4] = {wraw.x, wraw.y, wraw.z, wraw.w};
+    const uint32_t sv[4] = {sraw.x, sraw.y, sraw.z, sraw.w};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint16_t wb = static_cast<uint16_t>(wv[i >> 1] >> (16 * (i & 1)));
-    const uint16_t sb = static_cast<uint16_t>(sv[i >> 1] >> (16 * (i & 1)));
-    v[i] = f16_bits_to_f64(f64_to_f16_rn(f16_bits_to_f64(wb) * f16_bits_to_f64(sb)));
-    vmin = i == 0 ? v[i] : __builtin_fmin(vmin, v[i]);
-    vmax = i == 0 ? v[i] : __builtin_fmax(vmax, v[i]);
+    for (int i = 0; i < 8; ++i) {
+      const uint16_t wb = static_cast<uint16_t>(wv[i >> 1] >> (16 * (i & 1)));
+      const uint16_t sb = static_cast<uint16_t>(sv[i >> 1] >> (16 * (i & 1)));
+      v[i] = f16_bits_to_f64(f64_to_f16_rn(f16_bits_to_f64(wb) * f16_bits_to_f64(sb)));
+    }
+  };
+
+  double vmin = 0.0, vmax = 0.0;
+  for (int j = 0; j < nvec; ++j) {
+    double v[8];
+    fold8(j, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      vmin = (j == 0 && i == 0) ? v[i] : __builtin_fmin(vmin, v[i]);
+      vmax = (j == 0 && i == 0) ? v[i] : __builtin_fmax(vmax, v[i]);
+    }
   }
   // group extrema across the TPR lanes of this row (binary16 values: exact in float32)
   float fmin = static_cast<float>(vmin), fmax = static_cast<float>(vmax);
@@ -117,19 +128,24 @@ pack_kernel(const uint16_t* __restrict__ w, const uint16_t* __restrict__ s_c, in
     s = __builtin_fmax(s, 5.9604644775390625e-08);
     z = 8;
   }
-  // Codes. v/s is either an exact tie (k + 1/2) or at least 2^-41 away from one, so the
-  // float64 quotient rounds half-to-even exactly like the real quotient.
-  uint32_t word = 0;
+  // Codes (the fold recomputed: cheaper than holding a whole group per thread). v/s is
+  // either an exact tie (k + 1/2) or at least 2^-41 away from one, so the float64
+  // quotient rounds half-to-even exactly like the real quotient.
+  for (int j = 0; j < nvec; ++j) {
+    double v[8];
+    fold8(j, v);
+    uint32_t word = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int q = static_cast<int>(__builtin_rint(v[i] / s)) + z;
-    q = q < 0 ? 0 : (q > 15 ? 15 : q);
-    word |= static_cast<uint32_t>(q) << (4 * i);
+    for (int i = 0; i < 8; ++i) {
+      int q = static_cast<int>(__builtin_rint(v[i] / s)) + z;
+      q = q < 0 ? 0 : (q > 15 ? 15 : q);
+      word |= static_cast<uint32_t>(q) << (4 * i);
+    }
+    if (n < N)
+      qweight[static_cast<int64_t>(n) * (K / 8) + (static_cast<int64_t>(g) * group + (t + j * TPR) * 8) / 8] =
+          static_cast<int32_t>(word);
   }
-  if (n < N) {
-    qweight[static_cast<int64_t>(n) * (K / 8) + k0 / 8] = static_cast<int32_t>(word);
-    if (t == 0) scales[static_cast<int64_t>(g) * N + n] = f64_to_f16_rn(s);
-  }
+  if (n < N && t == 0) scales[static_cast<int64_t>(g) * N + n] = f64_to_f16_rn(s);
   if (fmt == 0) {
     __shared__ uint32_t zsh[8];
     if (t == 0) zsh[row_in_blk] = static_cast<uint32_t>(z);
@@ -157,10 +173,20 @@ hipError_t launch_channel_scale(const uint16_t* x_cal, int64_t rows, int64_t K, 
 hipError_t launch_pack(const uint16_t* w, const uint16_t* s_c, int64_t N, int64_t K,
                        int32_t group, int32_t fmt, int32_t* qweight, uint16_t* scales,
                        int32_t* qzeros, hipStream_t st) {
-  if (group != kGroup) return hipErrorInvalidValue;
-  dim3 grid(static_cast<unsigned>(N / 8), static_cast<unsigned>(K / group));
-  hipLaunchKernelGGL(pack_kernel<kGroup>, grid, dim3(8 * (kGroup / 8)), 0, st, w, s_c,
-                     static_cast<int>(K), fmt, qweight, scales, qzeros, static_cast<int>(N));
+  const dim3 grid(static_cast<unsigned>(N / 8), static_cast<unsigned>(K / group));
+  const int k = static_cast<int>(K), n = static_cast<int>(N), g = static_cast<int>(group);
+  if (group == 32) {
+    hipLaunchKernelGGL(pack_kernel<4>, grid, dim3(32), 0, st, w, s_c, k, g, fmt, qweight,
+                       scales, qzeros, n);
+  } else if (group == 64) {
+    hipLaunchKernelGGL(pack_kernel<8>, grid, dim3(64), 0, st, w, s_c, k, g, fmt, qweight,
+                       scales, qzeros, n);
+  } else if (group % kGroup == 0) {
+    hipLaunchKernelGGL(pack_kernel<16>, grid, dim3(128), 0, st, w, s_c, k, g, fmt, qweight,
+                       scales, qzeros, n);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

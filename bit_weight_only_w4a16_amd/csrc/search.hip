@@ -164,7 +164,7 @@ hipError_t launch_scale_search(const uint16_t* w, const uint16_t* x_cal, int64_t
     if ((e = launch_channel_scale(x_cal, rows, K, alpha, s_c, inv, st)) != hipSuccess) return e;
     if ((e = launch_pack(w, s_c, N, K, group, fmt, qweight, scales, qzeros, st)) != hipSuccess) return e;
     if ((e = launch_repack(qweight, scales, qzeros, N, K, group, fmt, packed, st)) != hipSuccess) return e;
-    if ((e = launch_gemm(x_cal, inv, packed, rows, N, K, fmt, yq, gws,
+    if ((e = launch_gemm(x_cal, inv, packed, rows, N, K, group, fmt, yq, gws,
                          static_cast<size_t>(L.gemm_ws_bytes), st)) != hipSuccess)
       return e;
     hipLaunchKernelGGL(loss_partial_kernel, dim3(kLossBlocks), dim3(256), 0, st, ref, yq,

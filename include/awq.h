@@ -25,9 +25,10 @@
  *                          (asymmetric format only; NULL for the symmetric format)
  *       X [M][K], y [M][N] binary16
  *   - Formats: AWQ_FMT_ASYM (scale + zero point), AWQ_FMT_SYM8 (zero fixed at 8).
- *   - Shapes: N % 8 == 0, K % group == 0, group == 128 (the only group size the
- *     kernels are built for; others return AWQ_ERR_UNSUPPORTED), N*K < 2^31,
- *     K <= 2^22, M*K < 2^32 and M*N < 2^32 (AWQ_ERR_UNSUPPORTED beyond).
+ *   - Shapes: N % 8 == 0, K % group == 0 (AWQ_ERR_INVALID_ARG otherwise); group 32,
+ *     64, or a multiple of 128 (per-channel: group == K), K % 128 == 0, N*K < 2^31,
+ *     K <= 2^22, M*K < 2^32 and M*N < 2^32 (AWQ_ERR_UNSUPPORTED otherwise). The pages
+ *     fix no group size ("group-wise", "blockwise"); 128 is the tuned case.
  *   - Pointers marked "device" must be device (HBM) addresses on the current HIP
  *     device, 16-byte aligned (AWQ_ERR_MISALIGNED otherwise). The library never
  *     allocates, frees or retains a pointer: the caller owns every buffer.
@@ -121,15 +122,18 @@ size_t awq_repacked_bytes(int64_t N, int64_t K, int32_t group, int32_t fmt);
 /*
  * awq_repack - canonical (qweight, scales, qzeros) to the gfx950 packed layout read
  * by awq_gemv, awq_gemm and awq_dequant(AWQ_LAYOUT_GFX950). A pure integer
- * permutation: no value changes. The layout (version awq_layout_version() == 2):
+ * permutation: no value changes. The layout (version awq_layout_version() == 3):
  *   rows padded to Np = 16 * ceil(N / 16) (padding rows: codes 0, scale 0, zero 0);
  *   codes  at offset 0: unit (t, g) for t < Np/16, g < K/128 at ((t * K/128) + g) * 1024;
  *          in a unit, lane l (0..63) owns bytes [16 l, 16 l + 16): row n = 16 t + l % 16,
  *          four words, word i holding channel k = 128 g + 32 (l / 16) + 8 i + e, e < 8,
  *          at nibble position (e >> 1) + 4 * (e & 1);
- *   scales at offset Np * K / 2: binary16 [(t * K/128 + g) * 16 + l % 16];
- *   zeros  (ASYM) at the next 256-byte boundary: 4-bit [(t * K/128 + g) * 16 + r],
- *          nibble (r % 8) of 32-bit word ((t * K/128 + g) * 2 + r / 8).
+ *   sets   each unit carries S = max(1, 128 / group) sets of 16 scales and zeros: set j
+ *          of unit g holds canonical group 128 g / group + j for group < 128 (lane l
+ *          uses set (l / 16) * S / 4), canonical group 128 g / group for group >= 128;
+ *   scales at offset Np * K / 2: binary16 [((t * K/128 + g) * S + j) * 16 + row % 16];
+ *   zeros  (ASYM) at the next 256-byte boundary: nibble (r % 8) of 32-bit word
+ *          ((t * K/128 + g) * S + j) * 2 + r / 8 for row r = row % 16 of set j.
  * One 128-bit load per lane of a wavefront reads a whole unit; a lane's word i is the
  * B operand of step i of v_mfma_f32_16x16x32_f16 for its row.
  * qweight, scales: device, read only. qzeros: device for ASYM, NULL for SYM8.

@@ -41,7 +41,7 @@ def test_status_strings(lib):
         s = awq.status_string(code)
         assert isinstance(s, str) and s
     assert awq.status_string(99) == "unknown status"
-    assert awq.awq_layout_version() == 2
+    assert awq.awq_layout_version() == 3
 
 
 def test_sizes():
@@ -50,7 +50,14 @@ def test_sizes():
     assert awq.awq_repacked_bytes(4096, 4096, 128, awq.FMT_SYM8) == 8388608 + 262144
     assert awq.awq_repacked_bytes(100, 256) == 0          # N % 8 != 0
     assert awq.awq_repacked_bytes(64, 200) == 0           # K % 128 != 0
-    assert awq.awq_repacked_bytes(64, 256, 64) == 0       # unsupported group
+    assert awq.awq_repacked_bytes(64, 384, 96) == 0       # unsupported group
+    assert awq.awq_repacked_bytes(64, 200, 8) == 0        # K not a multiple of 128
+    # groups of 64 / 32: two / four scale sets per 1 KiB unit; >= 128: one set per unit
+    # (4 tiles x 2 units: codes 8192 B; scales 4 x 2 x S x 32 B; zeros 4 x 2 x S x 8 B;
+    # regions 256-byte aligned)
+    assert awq.awq_repacked_bytes(64, 256, 64) == 8192 + 512 + 256
+    assert awq.awq_repacked_bytes(64, 256, 32) == 8192 + 1024 + 256
+    assert awq.awq_repacked_bytes(64, 256, 256) == awq.awq_repacked_bytes(64, 256, 128)
     assert awq.awq_workspace_bytes(0, 4096, 4096) == 0
     # split-K partial sums only where the output blocks alone leave CUs idle
     assert awq.awq_workspace_bytes(16, 4096, 4096) % (16 * 4096 * 4) == 0
@@ -80,7 +87,7 @@ P = 4096  # an aligned stand-in address; never dereferenced because validation f
     ((P, None, P, 1, 64, 100, 128, 0, P, None, 0, None), INVALID),         # K % group
     ((P, None, P, 1, 64, 128, 128, 2, P, None, 0, None), INVALID),         # fmt
     ((P, None, P, -1, 64, 128, 128, 0, P, None, 0, None), INVALID),        # M < 0
-    ((P, None, P, 1, 64, 256, 64, 0, P, None, 0, None), UNSUPPORTED),      # group 64
+    ((P, None, P, 1, 64, 384, 96, 0, P, None, 0, None), UNSUPPORTED),      # group 96
     ((P + 2, None, P, 1, 64, 128, 128, 0, P, None, 0, None), MISALIGNED),  # x
     ((P, P + 8, P, 1, 64, 128, 128, 0, P, None, 0, None), MISALIGNED),     # inv_s_c
     ((P, None, P, 1, 64, 128, 128, 0, P, None, 16, None), INVALID),        # ws NULL, bytes
@@ -94,7 +101,7 @@ def test_gemv_validation(lib, args, code):
 def test_gemm_validation(lib):
     assert lib.awq_gemm(None, None, None, 0, 64, 128, 128, 0, None, None, 0, None) == OK
     assert lib.awq_gemm(P, None, P, 9, 64, 100, 128, 0, P, None, 0, None) == INVALID
-    assert lib.awq_gemm(P, None, P, 9, 64, 256, 32, 0, P, None, 0, None) == UNSUPPORTED
+    assert lib.awq_gemm(P, None, P, 9, 64, 384, 96, 0, P, None, 0, None) == UNSUPPORTED
     assert lib.awq_gemm(P, None, P + 4, 9, 64, 128, 128, 0, P, None, 0, None) == MISALIGNED
 
 
@@ -162,7 +169,7 @@ def test_scale_search_validation(lib):
     assert call(a2=0) == INVALID                      # rows
     assert call(a2=257) == INVALID
     assert call(a7=0) == INVALID                      # grid
-    assert call(a5=64) == UNSUPPORTED                 # group
+    assert call(a5=16) == UNSUPPORTED                 # group 16
     assert call(a8=P + 4) == MISALIGNED               # losses
     assert call(a1=P + 2) == MISALIGNED               # x_cal
     assert call(a11=need - 1) == WORKSPACE

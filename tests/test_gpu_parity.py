@@ -38,24 +38,24 @@ def rel_err(y, y_ref):
     return np.max(np.abs(y - y_ref)) / max(np.max(np.abs(y_ref)), 1e-30)
 
 
-def gpu_quantize(w, x_cal, fmt, use_scale=True):
+def gpu_quantize(w, x_cal, fmt, use_scale=True, group=128):
     w_d = to_dev(w)
     s_c = inv = None
     if use_scale:
         s_c, inv = awq.awq_channel_scale(to_dev(x_cal), 0.5)
-    qweight, scales, qzeros = awq.awq_pack(w_d, s_c, 128, fmt)
+    qweight, scales, qzeros = awq.awq_pack(w_d, s_c, group, fmt)
     n, k = w.shape
-    packed = awq.awq_repack(qweight, scales, qzeros, n, k, 128, fmt)
+    packed = awq.awq_repack(qweight, scales, qzeros, n, k, group, fmt)
     return {"s_c": s_c, "inv": inv, "qweight": qweight, "scales": scales, "qzeros": qzeros,
             "packed": packed}
 
 
-def oracle_quantize(w, x_cal, fmt, use_scale=True, rows=None):
+def oracle_quantize(w, x_cal, fmt, use_scale=True, rows=None, group=128):
     s = inv = None
     if use_scale:
         s, inv = oracle.channel_scale(x_cal, 0.5)
     ww = w if rows is None else w[rows]
-    layer = oracle.quantize_layer(ww, s, 128, fmt)
+    layer = oracle.quantize_layer(ww, s, group, fmt)
     layer["s_c"], layer["inv"] = s, inv
     return layer
 
@@ -349,3 +349,50 @@ def test_scale_search_matches_oracle(fmt, rows):
     best2, losses2 = awq.awq_scale_search(to_dev(d["w"]), to_dev(x_cal), 128, fmt, grid)
     torch.cuda.synchronize()
     assert torch.equal(losses, losses2) and torch.equal(best, best2)
+
+
+# ----------------------------------------------------------------- group sizes
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("group", [32, 64, 256, "K"])
+@pytest.mark.parametrize("n,k", [(200, 1024), (72, 512)])
+def test_group_sizes(n, k, group, fmt):
+    """Groups of 32 / 64 channels (several scale sets per packed unit), 256 and
+    per-channel (one set per unit, repeated): packing and dequantization bit-exact in
+    both layouts, the decode and matrix-core products within tolerance."""
+    g_size = k if group == "K" else group
+    d = synth.layer_inputs(5, 16, n, k)
+    g = gpu_quantize(d["w"], d["x_cal"], fmt, group=g_size)
+    o = oracle_quantize(d["w"], d["x_cal"], fmt, group=g_size)
+    check_bits_exact(g, o, fmt)
+    for layout, w in ((awq.LAYOUT_CANONICAL, g["qweight"]), (awq.LAYOUT_GFX950, g["packed"])):
+        sc, qz = (g["scales"], g["qzeros"]) if layout == awq.LAYOUT_CANONICAL else (None, None)
+        wd = awq.awq_dequant(w, sc, qz, layout, n, k, g_size, fmt)
+        assert np.array_equal(bits(wd), f16bits(o["w_d"]))
+    for m in (1, 5, 16):
+        x = d["x"][:m]
+        y_ref = oracle.matmul_ref(x, o["w_d"], o["inv"])
+        ws = awq.workspace(m, n, k, DEV, g_size)
+        y = awq.awq_gemv(to_dev(x), g["inv"], g["packed"], n, k, g_size, fmt, ws=ws)
+        assert rel_err(y.cpu().numpy(), y_ref) <= TOL
+        y = awq.awq_gemm(to_dev(x), g["inv"], g["packed"], n, k, g_size, fmt, ws=ws)
+        assert rel_err(y.cpu().numpy(), y_ref) <= TOL
+    xl = synth.activations(300, k, 11, d["outliers"])                    # wide-tile GEMM
+    y_ref = oracle.matmul_ref(xl, o["w_d"], o["inv"])
+    y = awq.awq_gemm(to_dev(xl), g["inv"], g["packed"], n, k, g_size, fmt,
+                     ws=awq.workspace(300, n, k, DEV, g_size))
+    assert rel_err(y.cpu().numpy(), y_ref) <= TOL
+
+
+@pytest.mark.parametrize("group", [32, 64, "K"])
+def test_group_sizes_full_shape(group):
+    """4096 -> 11008 at M = 1 with the other group sizes, sampled output rows."""
+    n, k = 11008, 4096
+    g_size = k if group == "K" else group
+    d = synth.layer_inputs(1, 1, n, k)
+    g = gpu_quantize(d["w"], d["x_cal"], 0, group=g_size)
+    rows = np.concatenate([np.arange(8), np.arange(5000, 5008), np.arange(n - 8, n)])
+    o = oracle_quantize(d["w"], d["x_cal"], 0, rows=rows, group=g_size)
+    y = awq.awq_gemv(to_dev(d["x"]), g["inv"], g["packed"], n, k, g_size, 0).cpu().numpy()
+    y_ref = oracle.matmul_ref(d["x"], o["w_d"], o["inv"])
+    assert rel_err(y[:, rows], y_ref) <= TOL
