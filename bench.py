@@ -52,7 +52,6 @@ BATCHED_M = (8, 16, 32, 64)
 LAYERS_70B = [("up", 28672, 8192), ("down", 8192, 28672)]
 N_BLOCKS_7B = 32
 GEMV_MAX_M = 4  # above this the split-K matrix-core GEMM is faster (batched rows)
-DOMINANT = "gate"  # 4096 -> 11008: the largest share of the step's kernel time
 
 
 def parse():
@@ -202,11 +201,13 @@ def main():
         per_layer[shape_layer] = {"shape": f"{L['k']}->{L['n']}", "us": round(us, 3),
                                   "GB/s": round(L["bytes"] / us / 1e3, 1),
                                   "launches": 3 * reps * rot}
-    dom = next(L for L in layers if L["name"] == DOMINANT)
-    dom_us = per_layer[DOMINANT]["us"]
-    achieved = dom["bytes"] / dom_us / 1e3  # GB/s
+    # The dominant kernel is the decode kernel itself: its 7 launches are the whole step
+    # (the 4096 -> 4096 launches alone are 45 % of it). Roofline over one step: the
+    # algorithmic bytes of the 7 launches / their summed kernel time, i.e. bytes per
+    # launch / average launch duration.
     sum_kernel_us = 4 * per_layer["q"]["us"] + 2 * per_layer["gate"]["us"] + per_layer["down"]["us"]
-    traffic = measured_traffic(dom["bytes"])
+    achieved = step_bytes / sum_kernel_us / 1e3  # GB/s
+    traffic = measured_traffic()
     del copies, layers
     torch.cuda.empty_cache()
 
@@ -406,7 +407,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
                      "peak": rl.HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / rl.HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": f"awq_gemv 4096->11008 M=1 ({dom_us:.3f} us/launch)"},
+                     "kernel": f"awq_gemv M=1, the 7 launches of a step ({sum_kernel_us / 7:.3f} "
+                               f"us/launch average, {step_bytes / 7:.0f} B/launch average)"},
         "per_layer_kernel": per_layer,
         "kernel_sum_us_per_step": round(sum_kernel_us, 3),
         "kernel_only_GB/s": round(step_bytes / sum_kernel_us / 1e3, 1),
@@ -418,7 +420,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_4096x11008_m1_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_decode_step_m1_traffic.txt")
 GEMV_SOURCES = ("bit_weight_only_w4a16_amd/csrc/gemv.hip",
                 "bit_weight_only_w4a16_amd/csrc/awq_internal.hpp")
 
@@ -432,11 +434,11 @@ def gemv_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(algorithmic_bytes: int):
-    """HBM bytes per launch of the dominant GEMV, as measured by rocprofv3 counters
-    (FETCH_SIZE + WRITE_SIZE, each scaled by what it reads for a plain copy of known
-    size) and recorded with the hash of the kernel source; None if the kernel source
-    changed since, or if no measurement is recorded."""
+def measured_traffic():
+    """HBM bytes per launch (average over the 7 launches of a decode step) of the decode
+    kernel, as measured by rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, each scaled by
+    what it reads for a plain copy of known size) and recorded with the hash of the
+    kernel source; None if the kernel source changed since, or if none is recorded."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
