@@ -50,6 +50,7 @@ PREFILL_LAYERS = [("qkv", 6144, 4096), ("gate_up", 28672, 4096), ("down", 4096, 
 PREFILL_M = 2048
 BATCHED_M = (8, 16, 32, 64)
 LAYERS_70B = [("up", 28672, 8192), ("down", 8192, 28672)]
+M_70B = (16, 256, 4096)
 N_BLOCKS_7B = 32
 GEMV_MAX_M = 4  # above this the split-K matrix-core GEMM is faster (batched rows)
 
@@ -65,7 +66,7 @@ def parse():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip fused step, batched decode and 70B layers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     return ap.parse_args()
@@ -186,7 +187,19 @@ def main():
     t1 = time.perf_counter()
     sec = t1 - t0
     value_gbs = step_bytes * K / sec / 1e9
-    del g_all, g_one
+    # per-step spread (outside the timed region): each step graph between two events
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    for i, (ea, eb) in enumerate(evs):
+        ea.record()
+        g_one[i % rot].replay()
+        eb.record()
+    torch.cuda.synchronize()
+    per_step = sorted(ea.elapsed_time(eb) * 1e3 for ea, eb in evs)
+    step_spread = {"median": round(per_step[K // 2], 3),
+                   "p10": round(per_step[K // 10], 3),
+                   "p90": round(per_step[(9 * K) // 10], 3), "steps": K}
+    del g_all, g_one, evs
 
     # ------------------------------------------- per-kernel durations (HIP events)
     # One graph per layer shape holding that layer's GEMV over all its weight copies,
@@ -257,23 +270,39 @@ def main():
         del b_cp, bl, xall
         torch.cuda.empty_cache()
 
-        # -------------------------------------- 70B layers at M = 1
-        log("70B layers at M = 1")
-        rows70 = []
+        # -------------------------------------- 70B layers, M = 1, 16, 256, 4096
+        log("70B layers")
+        rows70, rows70b = [], []
         for fmt, fname in ((awq.FMT_ASYM, "asym"), (awq.FMT_SYM8, "sym")):
             for j, (name, n, k) in enumerate(LAYERS_70B):
-                L = make_layer(4, n, k, layer=j, fmt=fmt)
+                L = make_layer(4, n, k, m=max(M_70B), layer=j, fmt=fmt)
                 r70 = rotation(L["packed"].numel())
                 cp = [L["packed"]] + [L["packed"].clone() for _ in range(r70 - 1)]
-                ws = awq.workspace(1, n, k, dev)
-                us = graph_us([product(awq.awq_gemv, L, cp[r], ws) for r in range(r70)], 5)
-                byts = rl.algorithmic_bytes(1, n, k, GROUP, fmt, True)
-                rows70.append({"layer": name, "shape": f"{k}->{n}", "format": fname,
-                               "us": round(us, 3), "GB/s": round(byts / us / 1e3, 1),
-                               "frac": round(byts / us / 1e3 / rl.HBM_PEAK_GBS, 4)})
+                wbytes = rl.weight_bytes(n, k, GROUP, fmt)
+                for m in (1,) + M_70B:
+                    Lm = dict(L, m=m, x=L["x"][:m].contiguous(),
+                              y=torch.empty((m, n), dtype=torch.float16, device=dev))
+                    ws = awq.workspace(m, n, k, dev)
+                    fn = awq.awq_gemv if m <= GEMV_MAX_M else awq.awq_gemm
+                    nrot = r70 if m <= 64 else 2  # weights from HBM where bandwidth-bound
+                    us = graph_us([product(fn, Lm, cp[r % nrot], ws) for r in range(max(nrot, 2))],
+                                  5 if m < 4096 else 2)
+                    byts = rl.algorithmic_bytes(m, n, k, GROUP, fmt, True)
+                    row = {"layer": name, "shape": f"{k}->{n}", "format": fname, "M": m,
+                           "us": round(us, 3), "GB/s": round(byts / us / 1e3, 1),
+                           "TFLOP/s": round(rl.flops(m, n, k) / us / 1e6, 2),
+                           "weight_bytes_per_row": round(wbytes / m)}
+                    if m <= 64:
+                        row["bound"], row["frac"] = "hbm", round(byts / us / 1e3 / rl.HBM_PEAK_GBS, 4)
+                    else:
+                        row["bound"] = "mfma"
+                        row["frac"] = round(rl.flops(m, n, k) / us / 1e6 / rl.MFMA_F16_PEAK_TFLOPS, 4)
+                    (rows70 if m == 1 else rows70b).append(row)
+                    del Lm
                 del cp, L
                 torch.cuda.empty_cache()
         extra["llama70b_m1"] = rows70
+        extra["llama70b_batched"] = rows70b
 
         # -------------------------------------- group sizes (NEXT-4): 4096 -> 11008, M = 1
         log("group sizes")
@@ -394,6 +423,7 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(sec / K * 1e3, 5),
+        "step_us_spread": step_spread,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -453,7 +483,8 @@ def measured_traffic():
 
 
 def cpu_baseline(seconds: float):
-    """The CPU oracle (as it stands) on the dominant decode layer: dequantize + product."""
+    """The CPU oracle (as it stands) on the dominant decode layer: dequantize + product,
+    with BLAS on every host core this process may use (at most 16), and on one."""
     import oracle
     from bit_weight_only_w4a16_amd import synth
     from bit_weight_only_w4a16_amd import roofline as rl
@@ -464,21 +495,31 @@ def cpu_baseline(seconds: float):
     d = synth.layer_inputs(1, 1, n, k, layer=4)
     s, inv = oracle.channel_scale(d["x_cal"], 0.5)
     layer = oracle.quantize_layer(d["w"], s, GROUP, oracle.FMT_ASYM)
-    reps, t = 0, 0.0
-    with threadpool_limits(1):
-        while t < seconds or reps < 1:
-            t0 = time.perf_counter()
-            w_d = oracle.dequant_packed(layer["qweight"], layer["scales"], layer["qzeros"],
-                                        GROUP, oracle.FMT_ASYM)
-            oracle.matmul_ref(d["x"], w_d, inv)
-            t += time.perf_counter() - t0
-            reps += 1
     byts = rl.algorithmic_bytes(1, n, k, GROUP, rl.FMT_ASYM, with_inv=True)
-    return {"value": round(byts * reps / t / 1e9, 4), "unit": "GB/s", "cores": 1,
+
+    def timed(threads):
+        reps, t = 0, 0.0
+        with threadpool_limits(threads):
+            while t < seconds or reps < 1:
+                t0 = time.perf_counter()
+                w_d = oracle.dequant_packed(layer["qweight"], layer["scales"], layer["qzeros"],
+                                            GROUP, oracle.FMT_ASYM)
+                oracle.matmul_ref(d["x"], w_d, inv)
+                t += time.perf_counter() - t0
+                reps += 1
+        return reps, t
+
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    reps, t = timed(cores)
+    reps1, t1 = timed(1)
+    return {"value": round(byts * reps / t / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
             "sample": f"oracle dequant + float64 product of the 4096->11008 decode layer "
-                      f"(M=1), {reps} repetitions in {t:.1f} s, BLAS limited to 1 thread",
-            "ms_per_layer": round(t / reps * 1e3, 1)}
+                      f"(M=1), {reps} repetitions in {t:.1f} s, BLAS limited to {cores} "
+                      f"threads (the dequantization itself is single-threaded numpy)",
+            "ms_per_layer": round(t / reps * 1e3, 1),
+            "single_thread": {"value": round(byts * reps1 / t1 / 1e9, 4), "unit": "GB/s",
+                              "ms_per_layer": round(t1 / reps1 * 1e3, 1)}}
 
 
 if __name__ == "__main__":

@@ -69,7 +69,10 @@ hipError_t launch_gemv(const uint16_t* x, const uint16_t* inv_s_c, const void* p
                        int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt, uint16_t* y,
                        void* ws, size_t ws_bytes, hipStream_t st);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
-size_t gemm_wide_workspace_bytes(int64_t M, int64_t K);
+size_t gemm_wide_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// y = binary16(sum over s of part[s]), part [splits][mn] float32, in split order
+hipError_t launch_splitk_reduce(const float* part, int splits, int64_t mn, uint16_t* y,
+                                hipStream_t st);
 size_t scale_search_workspace_bytes(int64_t rows, int64_t N, int64_t K, int32_t group,
                                     int32_t fmt);
 hipError_t launch_scale_search(const uint16_t* w, const uint16_t* x_cal, int64_t rows,
@@ -77,7 +80,7 @@ hipError_t launch_scale_search(const uint16_t* w, const uint16_t* x_cal, int64_t
                                double* losses, double* best_alpha, void* ws, hipStream_t st);
 hipError_t launch_gemm_wide(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
                             int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt,
-                            uint16_t* y, void* ws, int cfg, hipStream_t st);
+                            uint16_t* y, void* ws, size_t ws_bytes, int cfg, hipStream_t st);
 hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
                        int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt, uint16_t* y,
                        void* ws, size_t ws_bytes, hipStream_t st);

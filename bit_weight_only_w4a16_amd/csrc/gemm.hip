@@ -298,12 +298,9 @@ hipError_t launch_tiles_fmt(GemmArgs a, hipStream_t st) {
   const unsigned blocks = static_cast<unsigned>(a.n_blocks_m) * static_cast<unsigned>(a.n_blocks_n);
   hipLaunchKernelGGL((gemm_kernel<WAVES_M, WM, WN, SCHED, ASYM>), dim3(blocks, a.splits),
                      dim3(kGThreads), lds, st, a);
-  if (a.splits > 1) {
-    const int64_t mn = static_cast<int64_t>(a.M) * a.N;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(static_cast<unsigned>((mn / 4 + 255) / 256)),
-                       dim3(256), 0, st, a.part, a.splits, mn, a.y);
-  }
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  return launch_splitk_reduce(a.part, a.splits, static_cast<int64_t>(a.M) * a.N, a.y, st);
 }
 
 // Output blocks of the default tiling for an M x N product (see launch_gemm).
@@ -327,12 +324,19 @@ hipError_t launch_tiles(GemmArgs a, hipStream_t st) {
 
 }  // namespace
 
+hipError_t launch_splitk_reduce(const float* part, int splits, int64_t mn, uint16_t* y,
+                                hipStream_t st) {
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(static_cast<unsigned>((mn / 4 + 255) / 256)),
+                     dim3(256), 0, st, part, splits, mn, y);
+  return hipGetLastError();
+}
+
 // Large M runs the wide-tile kernel, which needs X' in the workspace when inv_s_c is
 // given.
 constexpr int64_t kWideMinM = 256;
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M >= kWideMinM) return gemm_wide_workspace_bytes(M, K);
+  if (M >= kWideMinM) return gemm_wide_workspace_bytes(M, N, K);
   const int s = pick_splits(default_blocks(M, N, K), M, N, K, static_cast<int>(K / kGroup));
   return s > 1 ? static_cast<size_t>(s) * M * N * sizeof(float) : 0;
 }
@@ -341,13 +345,14 @@ hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* p
                        int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt, uint16_t* y,
                        void* ws, size_t ws_bytes, hipStream_t st) {
   // large M: wide wavefront tiles, X' from the workspace (or pre-scaled by the caller);
-  // AWQ_GEMM_WIDE = "0" keeps the narrow kernel, "<column tiles><K split>" (41, 42, 31,
-  // 32, 21, 22) forces a wide configuration (for tuning sweeps)
+  // AWQ_GEMM_WIDE = "0" keeps the narrow kernel, "[splits]<column tiles><K split>" (41,
+  // 42, 31, 32, 21, 22, 442, ...) forces a wide configuration (for tuning sweeps)
   const char* wide = getenv("AWQ_GEMM_WIDE");
-  const bool wide_ok = inv_s_c == nullptr || (ws != nullptr && ws_bytes >= gemm_wide_workspace_bytes(M, K));
+  const bool wide_ok =
+      inv_s_c == nullptr || (ws != nullptr && ws_bytes >= static_cast<size_t>(M) * K * 2);
   if (M >= kWideMinM && wide_ok && !(wide && wide[0] == '0')) {
     const int cfg = wide ? atoi(wide) : 0;
-    return launch_gemm_wide(x, inv_s_c, packed, M, N, K, group, fmt, y, ws, cfg, st);
+    return launch_gemm_wide(x, inv_s_c, packed, M, N, K, group, fmt, y, ws, ws_bytes, cfg, st);
   }
   const PackedLayout L = make_layout(N, K, group, fmt);
   GemmArgs a;

@@ -43,6 +43,8 @@ struct WideArgs {
   int64_t zeros_off;
   uint32_t packed_bytes;
   int M, N, K, n_groups, n_tiles, n_blocks_m, n_blocks_n, sets;
+  float* part;  // splits > 1: float32 partial sums [splits][M][N]
+  int splits;
 };
 
 __global__ void __launch_bounds__(256) prescale_kernel(const uint16_t* x, const uint16_t* inv,
@@ -77,10 +79,14 @@ __global__ void __launch_bounds__(256 * KS) gemm_wide_kernel(WideArgs a) {
   const int bm = bid % a.n_blocks_m, bn = bid / a.n_blocks_m;
   const int m_blk = bm * kBM, n_blk = bn * BN;
   const int ng = a.n_groups;
-  // this wavefront's groups [g0, g1); both halves run the same number of trips
-  const int g0 = half * ((a.n_groups + 1) / 2);
-  const int g1 = KS == 1 ? a.n_groups : min(a.n_groups, g0 + (a.n_groups + 1) / 2);
-  const int trips = KS == 1 ? a.n_groups : (a.n_groups + 1) / 2;
+  // this workgroup's units [ga, gb) (split blockIdx.y of K), then this wavefront's
+  // [g0, g1); both halves run the same number of trips
+  const int per = (ng + a.splits - 1) / a.splits;
+  const int ga = min(ng, static_cast<int>(blockIdx.y) * per), gb = min(ng, ga + per);
+  const int span = gb - ga, hspan = (span + 1) / 2;
+  const int g0 = ga + half * hspan;
+  const int g1 = KS == 1 ? gb : min(gb, g0 + hspan);
+  const int trips = KS == 1 ? span : hspan;
 
   // weights: one resource over the packed layer, per-tile SGPR offsets (tiles past the
   // last are clamped: their outputs are never stored)
@@ -228,6 +234,8 @@ __global__ void __launch_bounds__(256 * KS) gemm_wide_kernel(WideArgs a) {
     }
   }
 
+  // binary16 results, or with K split across workgroups this split's float32 sums
+  float* part = a.part + static_cast<int64_t>(blockIdx.y) * a.M * a.N;
 #pragma unroll
   for (int ms = 0; ms < WM; ++ms) {
 #pragma unroll
@@ -237,8 +245,12 @@ __global__ void __launch_bounds__(256 * KS) gemm_wide_kernel(WideArgs a) {
       for (int q = 0; q < 4; ++q) {
         const int m = m_blk + ms * 16 + 4 * p + q;
         if (m < a.M && n < a.N) {
-          a.y[static_cast<int64_t>(m) * a.N + n] =
-              __builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[ms][j][q]));
+          const int64_t o = static_cast<int64_t>(m) * a.N + n;
+          if (a.splits > 1) {
+            part[o] = acc[ms][j][q];
+          } else {
+            a.y[o] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[ms][j][q]));
+          }
         }
       }
     }
@@ -260,8 +272,11 @@ hipError_t launch_wide_fmt(WideArgs a, hipStream_t st) {
   a.n_blocks_m = (a.M + kBM - 1) / kBM;
   a.n_blocks_n = (a.N + BN - 1) / BN;
   const unsigned blocks = static_cast<unsigned>(a.n_blocks_m) * static_cast<unsigned>(a.n_blocks_n);
-  hipLaunchKernelGGL((gemm_wide_kernel<WN, KS, ASYM>), dim3(blocks), dim3(256 * KS), lds, st, a);
-  return hipGetLastError();
+  hipLaunchKernelGGL((gemm_wide_kernel<WN, KS, ASYM>), dim3(blocks, a.splits), dim3(256 * KS),
+                     lds, st, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  return launch_splitk_reduce(a.part, a.splits, static_cast<int64_t>(a.M) * a.N, a.y, st);
 }
 
 template <int WN, int KS>
@@ -272,31 +287,42 @@ hipError_t launch_wide(const WideArgs& a, hipStream_t st) {
 // Column tiles per wavefront and K split for an M x N product, aiming at two workgroups
 // per CU (from sweeps on MI355X): 128 x 256 workgroup tiles when they give that many;
 // else 128 x 192 tiles when N divides into them and they do; else, with at most one
-// 128 x 256 block per CU, K split in two inside the workgroup.
-void pick_wide(int64_t M, int64_t N, int& wn, int& ks) {
+// 128 x 256 block per CU, K split in two inside the workgroup, and when the blocks
+// cover fewer than half of the CUs, K split across floor(256 / blocks) workgroups as
+// well (float32 partial sums in the workspace; each split at least 4 units, at most 16).
+struct WidePick {
+  int wn, ks, splits;
+};
+WidePick pick_wide(int64_t M, int64_t N, int64_t K) {
   const int64_t mb = (M + kBM - 1) / kBM;
   const int64_t blocks4 = mb * ((N + 255) / 256), blocks3 = mb * ((N + 191) / 192);
-  wn = 4;
-  ks = 1;
-  if (blocks4 >= 512) return;
-  if (N % 192 == 0 && blocks3 >= 512) {
-    wn = 3;
-    return;
-  }
-  if (blocks4 <= 256) ks = 2;
+  if (blocks4 >= 512) return {4, 1, 1};
+  if (N % 192 == 0 && blocks3 >= 512) return {3, 1, 1};
+  if (blocks4 > 256) return {4, 1, 1};
+  int64_t s = 256 / blocks4;
+  s = s < K / (4 * kGroup) ? s : K / (4 * kGroup);
+  s = s < 16 ? s : 16;
+  return {4, 2, s < 2 ? 1 : static_cast<int>(s)};
 }
+
+inline int64_t align256(int64_t b) { return (b + 255) & ~int64_t{255}; }
 
 }  // namespace
 
-size_t gemm_wide_workspace_bytes(int64_t M, int64_t K) {
-  return static_cast<size_t>(M) * K * sizeof(uint16_t);
+// X' first ([M][K] binary16, 256-byte aligned), then the partial sums of a K split.
+size_t gemm_wide_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const WidePick w = pick_wide(M, N, K);
+  const int64_t part = w.splits > 1 ? static_cast<int64_t>(w.splits) * M * N * 4 : 0;
+  return static_cast<size_t>(align256(M * K * 2) + part);
 }
 
-// X' into the workspace when inv_s_c is given (ws must hold M * K binary16), then the
-// product. cfg = 10 * column tiles per wavefront + K split, or 0 for the default choice.
+// X' into the workspace when inv_s_c is given, then the product; the K split across
+// workgroups only when the workspace (ws_bytes) holds its partial sums as well.
+// cfg = 100 * splits + 10 * column tiles per wavefront + K split in the workgroup, or 0
+// for the default choice.
 hipError_t launch_gemm_wide(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
                             int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt,
-                            uint16_t* y, void* ws, int cfg, hipStream_t st) {
+                            uint16_t* y, void* ws, size_t ws_bytes, int cfg, hipStream_t st) {
   const PackedLayout L = make_layout(N, K, group, fmt);
   const uint16_t* xs = x;
   if (inv_s_c != nullptr) {
@@ -319,8 +345,17 @@ hipError_t launch_gemm_wide(const uint16_t* x, const uint16_t* inv_s_c, const vo
   a.n_groups = static_cast<int>(L.n_groups);
   a.n_tiles = static_cast<int>(L.n_tiles);
   a.sets = static_cast<int>(L.sets);
-  int wn = cfg / 10, ks = cfg % 10;
-  if (cfg == 0) pick_wide(M, N, wn, ks);
+  WidePick w = pick_wide(M, N, K);
+  if (cfg != 0) w = {(cfg / 10) % 10, cfg % 10, cfg >= 100 ? cfg / 100 : 1};
+  const int64_t part_off = align256(M * K * 2);
+  a.splits = 1;
+  a.part = nullptr;
+  if (w.splits > 1 && ws != nullptr &&
+      ws_bytes >= static_cast<size_t>(part_off + static_cast<int64_t>(w.splits) * M * N * 4)) {
+    a.splits = w.splits;
+    a.part = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + part_off);
+  }
+  const int wn = w.wn, ks = w.ks;
   if (wn == 4 && ks == 1) return launch_wide<4, 1>(a, st);
   if (wn == 4 && ks == 2) return launch_wide<4, 2>(a, st);
   if (wn == 3 && ks == 1) return launch_wide<3, 1>(a, st);

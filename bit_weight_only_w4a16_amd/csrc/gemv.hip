@@ -56,6 +56,24 @@ struct MvArgs {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+// v + (v from lane `ctrl` of the same 16-lane row), one data-parallel-primitive move
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                                0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a row, left in every lane of it: swap neighbours, swap pairs
+// (quad permutations [1,0,3,2] and [2,3,0,1]), then add the mirrored half-row and the
+// mirrored row. Every lane adds the same two operands at each step, so all 16 hold the
+// same bits. Four ALU operations with no LDS round trip.
+__device__ __forceinline__ float row_sum16(float v) {
+  v = dpp_add<0xB1>(v);
+  v = dpp_add<0x4E>(v);
+  v = dpp_add<0x141>(v);
+  return dpp_add<0x140>(v);
+}
+
 template <int M>
 struct XPass {
   uint4 x[M];
@@ -193,14 +211,11 @@ __global__ void __launch_bounds__(WAVES * 64) gemv_kernel(MvArgs a) {
       ov = __builtin_amdgcn_fdot2(as_h2(val.y), o64, ov, false);
       ov = __builtin_amdgcn_fdot2(as_h2(val.z), o1024, ov, false);
       ov = __builtin_amdgcn_fdot2(as_h2(val.w), o64, ov, false);
-#pragma unroll
-      for (int w = 1; w < 16; w <<= 1) {
-        sv += __shfl_xor(sv, w, 16);
-        ov += __shfl_xor(ov, w, 16);
-      }
+      sv = row_sum16(sv);
+      ov = row_sum16(ov);
       if (j < nj) {
         *reinterpret_cast<uint4*>(xs + m * PK + gl * kGroup + 8 * r) = val;
-        if (r == 0) {
+        if (!EXACT && r == 0) {
           ssum[m * PG + gl] = sv;
           osum[m * PG + gl] = ov;
         }

@@ -64,6 +64,10 @@ def test_sizes():
     assert awq.awq_workspace_bytes(16, 4096, 4096) > 0
     # large M: X' = X * inv_s_c formed once, M x K binary16
     assert awq.awq_workspace_bytes(2048, 4096, 4096) == 2048 * 4096 * 2
+    # M >= 256 with few output blocks: X' (256-byte aligned) then float32 sums of the
+    # K splits (2 x 32 blocks of 128 x 256: 256 / 64 = 4 splits; 2 x 112 blocks: none)
+    assert awq.awq_workspace_bytes(256, 8192, 28672) == 256 * 28672 * 2 + 4 * 256 * 8192 * 4
+    assert awq.awq_workspace_bytes(256, 28672, 8192) == 256 * 8192 * 2
 
 
 def test_padded_layout_size():

@@ -242,6 +242,23 @@ def test_gemm_parity(n, k, m, fmt):
     assert rel_err(y2.cpu().numpy(), y_ref) <= TOL
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("n,k,m", [(512, 4096, 256), (520, 8192, 300)])
+def test_wide_gemm_split_k(n, k, m, fmt):
+    """M >= 256 with too few 128 x 256 output blocks for the CUs: K is split across
+    workgroups (float32 partial sums in the workspace, summed in split order)."""
+    d, g, o, y_ref = product_case(n, k, m, fmt)
+    x = to_dev(d["x"])
+    ws = awq.workspace(m, n, k, DEV)
+    assert ws.numel() > m * k * 2          # room for X' and the partial sums
+    ys = [awq.awq_gemm(x, g["inv"], g["packed"], n, k, 128, fmt, ws=ws) for _ in range(3)]
+    for y in ys:
+        assert rel_err(y.cpu().numpy(), y_ref) <= TOL
+        assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
+    y1 = awq.awq_gemm(x, g["inv"], g["packed"], n, k, 128, fmt, ws=None)   # unsplit
+    assert rel_err(y1.cpu().numpy(), y_ref) <= TOL
+
+
 @pytest.mark.parametrize("m", [3, 300])
 def test_products_with_prescaled_activations(m):
     """inv_s_c NULL: the caller passes X' = X * inv_s_c already in binary16."""
@@ -275,7 +292,8 @@ def test_m_zero_is_a_no_op():
     awq.awq_gemm(x, None, g["packed"], n, k, y=y)
 
 
-@pytest.mark.parametrize("fn,m", [("gemv", 1), ("gemm", 96), ("gemm", 16), ("gemm", 512)])
+@pytest.mark.parametrize("fn,m", [("gemv", 1), ("gemm", 96), ("gemm", 16), ("gemm", 256),
+                                  ("gemm", 512)])
 def test_products_deterministic(fn, m):
     n, k = 4096, 4096
     d, g, o, y_ref = product_case(n, k, m, 0)
@@ -299,12 +317,19 @@ FULL = [
     ("batched_m8", 11008, 4096, 8, 0, "gemv"),
     ("batched_m16_gemv", 11008, 4096, 16, 0, "gemv"),
     ("batched_m16", 11008, 4096, 16, 0, "gemm"),
+    ("batched_m32", 11008, 4096, 32, 0, "gemm"),
     ("batched_m64", 11008, 4096, 64, 0, "gemm"),
     ("prefill_qkv_m2048", 6144, 4096, 2048, 0, "gemm"),
+    ("prefill_gateup_m2048", 28672, 4096, 2048, 0, "gemm"),
     ("prefill_down_m2048", 4096, 14336, 2048, 0, "gemm"),
     ("70b_up_sym_m1", 28672, 8192, 1, 1, "gemv"),
     ("70b_down_asym_m1", 8192, 28672, 1, 0, "gemv"),
+    ("70b_up_asym_m16_gemv", 28672, 8192, 16, 0, "gemv"),
+    ("70b_down_sym_m16", 8192, 28672, 16, 1, "gemm"),
     ("70b_up_asym_m256", 28672, 8192, 256, 0, "gemm"),
+    ("70b_down_sym_m256", 8192, 28672, 256, 1, "gemm"),
+    ("70b_up_sym_m4096", 28672, 8192, 4096, 1, "gemm"),
+    ("70b_down_asym_m4096", 8192, 28672, 4096, 0, "gemm"),
 ]
 
 
