@@ -162,7 +162,10 @@ int awq_dequant(const void* w, const uint16_t* scales, const int32_t* qzeros,
  *    workgroups, the float32 partial sums [splits][M][N] go to the workspace and a
  *    second kernel adds them in split order;
  *  - at M >= 256 with inv_s_c given: X' = binary16(X * inv_s_c) is formed once into the
- *    workspace ([M][K] binary16) and the wide-tile kernel streams it into LDS.
+ *    workspace ([M][K] binary16) and the wide-tile kernel streams it into LDS;
+ *  - at M >= 256 when the 128 x 256 output blocks cover fewer than half of the CUs: K is
+ *    also split across workgroups, with the float32 partial sums [splits][M][N] placed
+ *    after X' (at the next 256-byte boundary) and added in split order.
  * Every call that uses the workspace overwrites the part it uses, so it needs no
  * initialisation; calls that share one workspace must be ordered (same stream). With a
  * NULL workspace awq_gemm runs unsplit and scales X' inside the kernel: same accuracy,
