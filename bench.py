@@ -109,14 +109,22 @@ def main():
     def rotation(weight_bytes):
         return max(2, math.ceil(args.rotate_bytes / weight_bytes))
 
-    def graph_us(launches, reps, trials=3):
+    def graph_us(launches, reps, trials=3, warm_ms=20.0):
         """Per-launch microseconds of a graph of back-to-back launches, replayed `reps`
-        times between two events on the capture stream; median of `trials`."""
+        times between two events on the capture stream; median of `trials`. The graph
+        first runs for about `warm_ms` of GPU time, so that the clocks have settled at
+        their loaded level (the first milliseconds after an idle host phase run slower)."""
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for f in launches:
                 f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        for _ in range(min(2000, int(warm_ms * 1e-3 / max(e0.elapsed_time(e1) * 1e-3, 1e-6)))):
+            g.replay()
         torch.cuda.synchronize()
         ts = []
         for _ in range(trials):
@@ -286,7 +294,7 @@ def main():
                     fn = awq.awq_gemv if m <= GEMV_MAX_M else awq.awq_gemm
                     nrot = r70 if m <= 64 else 2  # weights from HBM where bandwidth-bound
                     us = graph_us([product(fn, Lm, cp[r % nrot], ws) for r in range(max(nrot, 2))],
-                                  5 if m < 4096 else 2)
+                                  5 if m < 4096 else 2, warm_ms=100.0 if m >= 256 else 20.0)
                     byts = rl.algorithmic_bytes(m, n, k, GROUP, fmt, True)
                     row = {"layer": name, "shape": f"{k}->{n}", "format": fname, "M": m,
                            "us": round(us, 3), "GB/s": round(byts / us / 1e3, 1),
@@ -362,7 +370,8 @@ def main():
             L = make_layer(3, n, k, m=PREFILL_M, layer=j)
             cp = [L["packed"], L["packed"].clone()]
             ws = awq.workspace(PREFILL_M, n, k, dev)
-            us = graph_us([product(awq.awq_gemm, L, cp[r % 2], ws) for r in range(6)], 3)
+            us = graph_us([product(awq.awq_gemm, L, cp[r % 2], ws) for r in range(6)], 3,
+                          warm_ms=150.0)
             fl = rl.flops(PREFILL_M, n, k)
             tot_flop += fl
             tot_us += us
@@ -378,7 +387,7 @@ def main():
                                 awq.FMT_ASYM, out=wd)
                 torch.matmul(xs, wd.t(), out=L["y"])
 
-            for _ in range(2):
+            for _ in range(max(2, int(150e3 / us))):  # about 150 ms, as for the fused GEMM
                 unfused_call()
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

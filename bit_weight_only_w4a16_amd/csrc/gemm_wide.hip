@@ -198,18 +198,25 @@ __global__ void __launch_bounds__(256 * KS) gemm_wide_kernel(WideArgs a) {
   // two groups per trip; while group g is multiplied from one buffer, A(g + 1) streams
   // into the other and B(g + 1) into registers; one barrier per group (every wavefront
   // of the workgroup takes the same number of trips, so the barriers match)
+  // the multiply runs at raised wavefront priority: a wavefront that has its operands
+  // keeps the matrix core while the other wavefronts of the SIMD wait at the barrier or
+  // issue their loads, which keeps the wavefronts of a SIMD out of phase
   for (int t = 0; t < trips; t += 2) {
     const int g = g0 + t;
     dma_a(g + 1, 1);
     load_b(b1, g + 1);
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
     if (g < g1) compute(b0, 0);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     dma_a(g + 2, 0);
     load_b(b0, g + 2);
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
     if (g + 1 < g1) compute(b1, 1);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
