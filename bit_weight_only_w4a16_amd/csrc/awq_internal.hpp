@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace awq {
 
 // ---------------------------------------------------------------- layout constants
@@ -48,6 +50,21 @@ inline PackedLayout make_layout(int64_t N, int64_t K, int32_t group, int32_t fmt
 
 // the scale / zero set lane (r, p) of a unit uses: p * S / 4 for S sets per unit
 __host__ __device__ inline int lane_set(int p, int sets) { return (p * sets) >> 2; }
+
+// ------------------------------------------------------------ launch helpers
+// Raise a kernel's dynamic-LDS limit to `bytes` on the current device, once per device
+// (the attribute is held per device); `done` is that kernel's bit set of devices done.
+// Safe to call from several host threads: at worst two of them set the same value.
+inline hipError_t ensure_lds_limit(const void* kernel, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t{1} << dev : 0;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 // ------------------------------------------------------------ launchers (per file)
 hipError_t launch_channel_scale(const uint16_t* x_cal, int64_t rows, int64_t K, double alpha,

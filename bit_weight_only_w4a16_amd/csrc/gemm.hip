@@ -267,17 +267,17 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* part, i
   *reinterpret_cast<uint2*>(y + i) = make_uint2(as_u32(lo), as_u32(hi));
 }
 
-// Splits of K for a launch of `blocks` output blocks: enough workgroups to cover the
-// 256 CUs about twice when the output alone gives fewer than 256, each split at least two
-// groups, and the partial sums' traffic (written once, read once) no more than the
-// weights' bytes.
+// Splits of K for a launch of `blocks` output blocks (from sweeps on MI355X): about 640
+// workgroups (2.5 per CU) when the output alone gives fewer than 512, each split at least
+// 8 units, at most 8 splits, and the partial sums' traffic (written once, read once) no
+// more than the weights' bytes.
 int pick_splits(int64_t blocks, int64_t M, int64_t N, int64_t K, int n_groups) {
-  if (blocks >= 256) return 1;
-  int64_t s = (512 + blocks - 1) / blocks;
-  s = s < n_groups / 2 ? s : n_groups / 2;
+  if (blocks >= 512) return 1;
+  int64_t s = (640 + blocks - 1) / blocks;
+  s = s < n_groups / 8 ? s : n_groups / 8;
   const int64_t traffic_cap = K / (16 * M);  // 8 S M N <= N K / 2
   s = s < traffic_cap ? s : traffic_cap;
-  s = s < 16 ? s : 16;
+  s = s < 8 ? s : 8;
   return s < 1 ? 1 : static_cast<int>(s);
 }
 
@@ -285,14 +285,11 @@ template <int WAVES_M, int WM, int WN, int SCHED, bool ASYM>
 hipError_t launch_tiles_fmt(GemmArgs a, hipStream_t st) {
   constexpr int BM = WAVES_M * WM * 16, BN = (4 / WAVES_M) * WN * 16;
   const size_t lds = 2ull * BM * kLdsStride * sizeof(_Float16);
-  static bool attr_set = false;  // benign race: every thread sets the same value
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<WAVES_M, WM, WN, SCHED, ASYM>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_done{0};
+  const hipError_t ea = ensure_lds_limit(
+      reinterpret_cast<const void*>(&gemm_kernel<WAVES_M, WM, WN, SCHED, ASYM>), static_cast<int>(lds),
+      lds_done);
+  if (ea != hipSuccess) return ea;
   a.n_blocks_m = (a.M + BM - 1) / BM;
   a.n_blocks_n = (a.N + BN - 1) / BN;
   const unsigned blocks = static_cast<unsigned>(a.n_blocks_m) * static_cast<unsigned>(a.n_blocks_n);
@@ -310,7 +307,8 @@ int64_t blocks_of(int64_t M, int64_t N) {
   return ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
 }
 int64_t default_blocks(int64_t M, int64_t N, int64_t K) {
-  if (M <= 16) return blocks_of<1, 1, 2>(M, N);
+  if (M <= 32 && N * K <= (int64_t{1} << 26)) return blocks_of<1, 1, 1>(M, N);
+  if (M <= 32) return blocks_of<1, 1, 2>(M, N);
   if (M <= 64) return blocks_of<1, 4, 2>(M, N);
   if (K >= 8192 || N >= 16384) return blocks_of<1, 8, 2>(M, N);
   return blocks_of<1, 4, 4>(M, N);
@@ -373,7 +371,13 @@ hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* p
   // for the partial sums (without one the product runs unsplit)
   a.splits = 1;
   a.part = nullptr;
-  const int want = pick_splits(default_blocks(M, N, K), M, N, K, a.n_groups);
+  int want = pick_splits(default_blocks(M, N, K), M, N, K, a.n_groups);
+  // AWQ_GEMM_SPLITS = "<splits>" forces the K split (for tuning sweeps; needs a workspace
+  // of splits * M * N * 4 bytes, else the product runs unsplit)
+  if (const char* sp = getenv("AWQ_GEMM_SPLITS")) {
+    const int v = atoi(sp);
+    if (v >= 1 && v <= 16 && v <= a.n_groups) want = v;
+  }
   if (want > 1 && ws != nullptr && ws_bytes >= static_cast<size_t>(want) * M * N * sizeof(float)) {
     a.splits = want;
     a.part = static_cast<float*>(ws);
@@ -399,10 +403,13 @@ hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* p
     if (wv == 1 && wm == 1 && wn == 1 && sc == 0) return launch_tiles<1, 1, 1, 0>(a, st);
   }
   // Defaults from sweeps on MI355X: at M <= 64 the product is bound by streaming the
-  // weights, and narrow 64 x 128 workgroup tiles give the most workgroups; at larger M a
-  // 64 x 256 tile (each wavefront 64 x 64) runs best, or for long K or wide N a 128 x 128
-  // tile (each wavefront 128 x 32), which dequantizes each weight fragment for 8 row tiles.
-  if (M <= 16) return launch_tiles<1, 1, 2>(a, st);
+  // weights, and narrow workgroup tiles give the most workgroups (16 x 64 up to M = 32 for
+  // layers of at most 2^26 weights, else 16 x 128; 64 x 128 up to M = 64), K split so that
+  // the workgroups cover the CUs about 2.5 times; at larger M a 64 x 256 tile (each wavefront
+  // 64 x 64) runs best, or for long K or wide N a 128 x 128 tile (each wavefront 128 x
+  // 32), which dequantizes each weight fragment for 8 row tiles.
+  if (M <= 32 && N * K <= (int64_t{1} << 26)) return launch_tiles<1, 1, 1>(a, st);
+  if (M <= 32) return launch_tiles<1, 1, 2>(a, st);
   if (M <= 64) return launch_tiles<1, 4, 2>(a, st);
   if (K >= 8192 || N >= 16384) return launch_tiles<1, 8, 2>(a, st);
   return launch_tiles<1, 4, 4>(a, st);

@@ -268,14 +268,10 @@ template <int WN, int KS, bool ASYM>
 hipError_t launch_wide_fmt(WideArgs a, hipStream_t st) {
   constexpr int BN = 4 * WN * 16;
   const size_t lds = 2ull * KS * kTileBytes;
-  static bool attr_set = false;  // benign race: every thread sets the same value
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_wide_kernel<WN, KS, ASYM>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_done{0};
+  const hipError_t ea = ensure_lds_limit(reinterpret_cast<const void*>(&gemm_wide_kernel<WN, KS, ASYM>),
+                                         static_cast<int>(lds), lds_done);
+  if (ea != hipSuccess) return ea;
   a.n_blocks_m = (a.M + kBM - 1) / kBM;
   a.n_blocks_n = (a.N + BN - 1) / BN;
   const unsigned blocks = static_cast<unsigned>(a.n_blocks_m) * static_cast<unsigned>(a.n_blocks_n);

@@ -288,14 +288,11 @@ size_t smem_bytes(int M, int phase_groups, int waves) {
 template <int M, int WAVES, int BATCH, bool ASYM, bool EXACT>
 hipError_t launch_fmt(const MvArgs& a, int64_t n_tiles, hipStream_t st) {
   const size_t lds = smem_bytes(M, a.phase_groups, WAVES);
-  static bool attr_set = false;  // benign race: every thread sets the same value
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemv_kernel<M, WAVES, BATCH, ASYM, EXACT>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsAlone + 4 * WAVES * M * kTileN);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_done{0};
+  const hipError_t ea = ensure_lds_limit(
+      reinterpret_cast<const void*>(&gemv_kernel<M, WAVES, BATCH, ASYM, EXACT>),
+      kLdsAlone + 4 * WAVES * M * kTileN, lds_done);
+  if (ea != hipSuccess) return ea;
   hipLaunchKernelGGL((gemv_kernel<M, WAVES, BATCH, ASYM, EXACT>), dim3(static_cast<unsigned>(n_tiles)),
                      dim3(WAVES * 64), lds, st, a);
   return hipGetLastError();

@@ -231,7 +231,7 @@ def test_gemv_parity(n, k, m, fmt):
 
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("m", [1, 7, 16, 33, 64, 130, 256, 300])
-@pytest.mark.parametrize("n,k", [(512, 512), (200, 1024), (72, 256)])
+@pytest.mark.parametrize("n,k", [(512, 512), (200, 1024), (72, 256), (200, 2048)])
 def test_gemm_parity(n, k, m, fmt):
     d, g, o, y_ref = product_case(n, k, m, fmt)
     x = to_dev(d["x"])
