@@ -97,6 +97,23 @@ def _opt(t, name, dtype) -> int | None:
     return None if t is None else _dev(t, name, dtype)
 
 
+def _shape(t, name, shape) -> None:
+    """The library sees raw pointers: every buffer's extent is checked here."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _at_least(t, name, nbytes: int) -> None:
+    if t is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {nbytes}")
+
+
+def _same_device(ref: torch.Tensor, **named) -> None:
+    for name, t in named.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
 def _stream(device=None) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -127,6 +144,10 @@ def awq_pack(w: torch.Tensor, s_c: torch.Tensor | None = None, group: int = GROU
         raise ValueError("w must be [N, K]")
     n, k = w.shape
     dev = w.device
+    _shape(s_c, "s_c", (k,))
+    _same_device(w, s_c=s_c)
+    if group <= 0 or k % group != 0:
+        raise ValueError("group must divide K")
     qweight = torch.empty((n, k // 8), dtype=torch.int32, device=dev)
     scales = torch.empty((k // group, n), dtype=torch.float16, device=dev)
     qzeros = torch.empty((k // group, n // 8), dtype=torch.int32, device=dev) if fmt == FMT_ASYM else None
@@ -146,6 +167,10 @@ def awq_repack(qweight, scales, qzeros, n: int, k: int, group: int = GROUP,
     nbytes = awq_repacked_bytes(n, k, group, fmt)
     if nbytes == 0:
         raise ValueError("invalid layer shape")
+    _shape(qweight, "qweight", (n, k // 8))
+    _shape(scales, "scales", (k // group, n))
+    _shape(qzeros, "qzeros", (k // group, n // 8))
+    _same_device(qweight, scales=scales, qzeros=qzeros)
     packed = torch.empty(nbytes, dtype=torch.uint8, device=qweight.device)
     _check(lib().awq_repack(_dev(qweight, "qweight", torch.int32),
                             _dev(scales, "scales", torch.float16),
@@ -159,7 +184,15 @@ def awq_dequant(w, scales, qzeros, layout: int, n: int, k: int, group: int = GRO
     """W_d fp16 [N, K] from the canonical (layout 0) or gfx950 (layout 1) format."""
     if out is None:
         out = torch.empty((n, k), dtype=torch.float16, device=w.device)
+    _shape(out, "out", (n, k))
     wdt = torch.int32 if layout == LAYOUT_CANONICAL else torch.uint8
+    if layout == LAYOUT_CANONICAL and k % 8 == 0 and group > 0 and k % group == 0:
+        _shape(w, "w", (n, k // 8))
+        _shape(scales, "scales", (k // group, n))
+        _shape(qzeros, "qzeros", (k // group, n // 8))
+    elif layout == LAYOUT_GFX950:
+        _at_least(w, "packed", awq_repacked_bytes(n, k, group, fmt))
+    _same_device(w, scales=scales, qzeros=qzeros, out=out)
     _check(lib().awq_dequant(_dev(w, "w", wdt), _opt(scales, "scales", torch.float16),
                              _opt(qzeros, "qzeros", torch.int32), layout, n, k, group, fmt,
                              _dev(out, "out", torch.float16), _stream(w.device)), "awq_dequant")
@@ -178,6 +211,10 @@ def _product(fn_name, x, inv_s_c, packed, n, k, group, fmt, y, ws):
         raise ValueError("x must have K columns")
     if y is None:
         y = torch.empty((m, n), dtype=torch.float16, device=x.device)
+    _shape(y, "y", (m, n))
+    _shape(inv_s_c, "inv_s_c", (k,))
+    _at_least(packed, "packed", awq_repacked_bytes(n, k, group, fmt))
+    _same_device(x, inv_s_c=inv_s_c, packed=packed, y=y, ws=ws)
     ws_ptr, ws_bytes = (None, 0) if ws is None else (_dev(ws, "ws", torch.uint8), ws.numel())
     rc = getattr(lib(), fn_name)(_dev(x, "x", torch.float16), _opt(inv_s_c, "inv_s_c", torch.float16),
                                  _dev(packed, "packed", torch.uint8), m, n, k, group, fmt,
@@ -207,10 +244,13 @@ def awq_scale_search(w, x_cal, group: int = GROUP, fmt: int = FMT_ASYM, grid: in
                      ws=None):
     """AWQ exponent search on the device: (best_alpha [1] float64, losses [grid+1]
     float64), both device tensors, valid once the current stream is synchronised."""
+    if w.dim() != 2 or x_cal.dim() != 2:
+        raise ValueError("w must be [N, K] and x_cal [rows, K]")
     n, k = w.shape
     rows = x_cal.shape[0]
-    if x_cal.dim() != 2 or x_cal.shape[1] != k:
+    if x_cal.shape[1] != k:
         raise ValueError("x_cal must be [rows, K] with the weights' K")
+    _same_device(w, x_cal=x_cal, ws=ws)
     need = awq_scale_search_workspace_bytes(rows, n, k, group, fmt)
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=w.device)

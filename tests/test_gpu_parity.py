@@ -421,3 +421,28 @@ def test_group_sizes_full_shape(group):
     y = awq.awq_gemv(to_dev(d["x"]), g["inv"], g["packed"], n, k, g_size, 0).cpu().numpy()
     y_ref = oracle.matmul_ref(d["x"], o["w_d"], o["inv"])
     assert rel_err(y[:, rows], y_ref) <= TOL
+
+
+# ------------------------------------------------------- binding: extents checked on the host
+
+def test_binding_rejects_wrong_extents():
+    """The library sees raw pointers; the binding checks every buffer's extent before a
+    launch, so a wrong shape raises instead of reading or writing past a buffer."""
+    n, k = 256, 512
+    g = gpu_quantize(synth.weights(n, k, 3), np.ones((32, k), np.float16), 0)
+    x = torch.zeros((4, k), dtype=torch.float16, device=DEV)
+    for fn in (awq.awq_gemv, awq.awq_gemm):
+        with pytest.raises(ValueError):
+            fn(x, g["inv"], g["packed"], n, k, y=torch.empty((4, n - 8), dtype=torch.float16, device=DEV))
+        with pytest.raises(ValueError):
+            fn(x, g["inv"][: k - 8].contiguous(), g["packed"], n, k)
+        with pytest.raises(ValueError):
+            fn(x, g["inv"], g["packed"][:-256].contiguous(), n, k)
+        with pytest.raises(ValueError):
+            fn(x[:, : k - 128].contiguous(), g["inv"], g["packed"], n, k)
+    with pytest.raises(ValueError):
+        awq.awq_dequant(g["packed"], None, None, awq.LAYOUT_GFX950, n, k,
+                        out=torch.empty((n, k - 8), dtype=torch.float16, device=DEV))
+    with pytest.raises(ValueError):
+        awq.awq_repack(g["qweight"][:, :-1].contiguous(), g["scales"], g["qzeros"], n, k)
+    torch.cuda.synchronize()
