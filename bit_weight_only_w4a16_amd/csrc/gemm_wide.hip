@@ -292,7 +292,9 @@ hipError_t launch_wide(const WideArgs& a, hipStream_t st) {
 // else 128 x 192 tiles when N divides into them and they do; else, with at most one
 // 128 x 256 block per CU, K split in two inside the workgroup, and when the blocks
 // cover fewer than half of the CUs, K split across floor(256 / blocks) workgroups as
-// well (float32 partial sums in the workspace; each split at least 4 units, at most 16).
+// well (float32 partial sums in the workspace; each split at least 4 units, at most
+// 16). In that last case 128 x 192 tiles are taken instead when they fill more of the
+// 256 CUs (ragged N: 4096 -> 11008 at M = 256 and 512).
 struct WidePick {
   int wn, ks, splits;
 };
@@ -302,10 +304,18 @@ WidePick pick_wide(int64_t M, int64_t N, int64_t K) {
   if (blocks4 >= 512) return {4, 1, 1};
   if (N % 192 == 0 && blocks3 >= 512) return {3, 1, 1};
   if (blocks4 > 256) return {4, 1, 1};
-  int64_t s = 256 / blocks4;
-  s = s < K / (4 * kGroup) ? s : K / (4 * kGroup);
-  s = s < 16 ? s : 16;
-  return {4, 2, s < 2 ? 1 : static_cast<int>(s)};
+  auto splits_for = [&](int64_t blocks) {
+    int64_t s = 256 / blocks;
+    s = s < K / (4 * kGroup) ? s : K / (4 * kGroup);
+    s = s < 16 ? s : 16;
+    return s < 1 ? int64_t{1} : s;
+  };
+  const int64_t s4 = splits_for(blocks4);
+  if (blocks3 <= 256) {
+    const int64_t s3 = splits_for(blocks3);
+    if (blocks3 * s3 > blocks4 * s4) return {3, 2, s3 < 2 ? 1 : static_cast<int>(s3)};
+  }
+  return {4, 2, s4 < 2 ? 1 : static_cast<int>(s4)};
 }
 
 inline int64_t align256(int64_t b) { return (b + 255) & ~int64_t{255}; }
