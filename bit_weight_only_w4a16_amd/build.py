@@ -77,7 +77,34 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_abi_check(verbose)
     return LIB
+
+
+ABI_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi", "abi_check.c")
+ABI_CHECK_BIN = os.path.join(ROOT, "tests", "c_abi", "abi_check")
+
+
+def abi_check_command(out: str) -> list:
+    """gcc line for the plain-C user of the library (C99 against include/awq.h, linked
+    with the built library and the HIP runtime)."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(rocm, "include"),
+            ABI_CHECK_SRC, "-o", out, "-L", PKG, "-lawq_gfx950",
+            "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-lm",
+            f"-Wl,-rpath,{PKG}", f"-Wl,-rpath,{os.path.join(rocm, 'lib')}"]
+
+
+def build_abi_check(verbose: bool = False) -> str:
+    """Compile the C ABI check program (run by the GPU tests) next to its source."""
+    cmd = abi_check_command(ABI_CHECK_BIN)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"C ABI check failed to build:\n{r.stdout}\n{r.stderr}")
+    return ABI_CHECK_BIN
 
 
 def main() -> None:
