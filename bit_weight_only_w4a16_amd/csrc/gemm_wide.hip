@@ -175,14 +175,22 @@ __global__ void __launch_bounds__(256 * KS) gemm_wide_kernel(WideArgs a) {
         dequant_word(w, nz1024[j], nz64[j], s2[j], d);
         bf[j] = half8_t{d[0].x, d[0].y, d[1].x, d[1].y, d[2].x, d[2].y, d[3].x, d[3].y};
       }
-      // A fragment of row tile ms, k-step i: row 16 ms + r, chunk 4 p + i (swizzled)
+      // A fragment of row tile ms, k-step i: row 16 ms + r, chunk 4 p + i (swizzled);
+      // each is read two row tiles ahead of its matrix instructions (a ring of three),
+      // so the LDS latency overlaps the matrix core's work on the tiles before it
       const int chunk = (4 * p + i) ^ r;
+      auto afrag = [&](int ms) {
+        return *reinterpret_cast<const half8_t*>(src + (16 * ms + r) * kRowBytes + 16 * chunk);
+      };
+      half8_t af[3];
+      af[0] = afrag(0);
+      af[1] = afrag(1);
 #pragma unroll
       for (int ms = 0; ms < WM; ++ms) {
-        const half8_t af = *reinterpret_cast<const half8_t*>(src + (16 * ms + r) * kRowBytes + 16 * chunk);
+        if (ms + 2 < WM) af[(ms + 2) % 3] = afrag(ms + 2);
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
-          acc[ms][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[j], acc[ms][j], 0, 0, 0);
+          acc[ms][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[ms % 3], bf[j], acc[ms][j], 0, 0, 0);
         }
       }
     }
