@@ -298,23 +298,33 @@ hipError_t launch_fmt(const MvArgs& a, int64_t n_tiles, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The per-group correction needs the activation sums O and S of every row: from five
+// rows on, staging them costs more than dequantizing each weight exactly, so M > 4 (and
+// groups of 32 or 64) take the exact form.
 template <int M, int WAVES, int BATCH>
 hipError_t launch_cfg(const MvArgs& a, int64_t n_tiles, hipStream_t st) {
   const bool asym = a.zeros_off >= 0;
-  if (a.sets > 1) {
+  if (M > 4 || a.sets > 1) {
     return asym ? launch_fmt<M, WAVES, BATCH, true, true>(a, n_tiles, st)
                 : launch_fmt<M, WAVES, BATCH, false, true>(a, n_tiles, st);
   }
-  return asym ? launch_fmt<M, WAVES, BATCH, true, false>(a, n_tiles, st)
-              : launch_fmt<M, WAVES, BATCH, false, false>(a, n_tiles, st);
+  if constexpr (M <= 4) {
+    return asym ? launch_fmt<M, WAVES, BATCH, true, false>(a, n_tiles, st)
+                : launch_fmt<M, WAVES, BATCH, false, false>(a, n_tiles, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 // From sweeps on MI355X (4096 <= K, N <= 28672): long rows on few tiles (K >= 8192,
 // N <= 8192, so at most two workgroups per CU) take 16 wavefronts with one group in
-// flight each; everything else eight wavefronts with one group each.
+// flight each; everything else eight wavefronts with one group each. Sixteen
+// wavefronts leave 128 VGPRs per lane, which the staging of more than four activation
+// rows overflows (spills to scratch), so M > 4 always takes eight.
 template <int M>
 hipError_t launch_m(const MvArgs& a, int64_t n_tiles, hipStream_t st) {
-  if (a.n_groups >= 64 && n_tiles <= 512) return launch_cfg<M, 16, 1>(a, n_tiles, st);
+  if constexpr (M <= 4) {
+    if (a.n_groups >= 64 && n_tiles <= 512) return launch_cfg<M, 16, 1>(a, n_tiles, st);
+  }
   return launch_cfg<M, 8, 1>(a, n_tiles, st);
 }
 

@@ -230,6 +230,17 @@ def test_gemv_parity(n, k, m, fmt):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("n,k,m", [(64, 5120, 16), (64, 5632, 13), (128, 9216, 8),
+                                   (48, 13312, 16), (40, 15360, 5)])
+def test_gemv_parity_long_rows(n, k, m, fmt):
+    """Rows long enough that the staged activations of all groups do not fit in LDS at
+    once: the decode kernel walks K in several phases."""
+    d, g, o, y_ref = product_case(n, k, m, fmt)
+    y = awq.awq_gemv(to_dev(d["x"]), g["inv"], g["packed"], n, k, 128, fmt)
+    assert rel_err(y.cpu().numpy(), y_ref) <= TOL
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("m", [1, 7, 16, 33, 64, 130, 256, 300])
 @pytest.mark.parametrize("n,k", [(512, 512), (200, 1024), (72, 256), (200, 2048)])
 def test_gemm_parity(n, k, m, fmt):
@@ -325,6 +336,8 @@ FULL = [
     ("70b_up_sym_m1", 28672, 8192, 1, 1, "gemv"),
     ("70b_down_asym_m1", 8192, 28672, 1, 0, "gemv"),
     ("70b_up_asym_m16_gemv", 28672, 8192, 16, 0, "gemv"),
+    ("7b_down_m8_gemv", 4096, 11008, 8, 0, "gemv"),
+    ("7b_down_m16_gemv", 4096, 11008, 16, 0, "gemv"),
     ("70b_down_sym_m16", 8192, 28672, 16, 1, "gemm"),
     ("70b_up_asym_m256", 28672, 8192, 256, 0, "gemm"),
     ("70b_down_sym_m256", 8192, 28672, 256, 1, "gemm"),
