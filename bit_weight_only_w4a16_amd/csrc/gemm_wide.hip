@@ -21,7 +21,8 @@
 //    load fall in 16 different bank groups.
 //  * Activation tiles are double-buffered in LDS (2 x 32 KiB), one barrier per group; the
 //    weights of the next group are in registers while a group is multiplied; every load
-//    is issued unconditionally (a group past the end reads zeros).
+//    is issued unconditionally: a prefetch past the wavefront's last group re-reads that
+//    group (an L2 hit, never multiplied), so no load needs a per-lane offset of its own.
 //  * Four wavefronts side by side along N: a workgroup covers 128 x 256 outputs (or
 //    128 x 192 / 128 x 128 with three / two column tiles per wavefront); accumulators in
 //    VGPRs. With few output blocks, eight wavefronts split K in two (see KS below).
@@ -120,15 +121,13 @@ __global__ void __launch_bounds__(256 * KS) gemm_wide_kernel(WideArgs a) {
     a_voff[j] = static_cast<uint32_t>(row * a.K + 8 * chunk) * 2;
   }
   auto dma_a = [&](int g, int buf) {
-    const bool live = g < g1;
-    const uint32_t skip = live ? 0u : kNoLoad;
-    const int soff = live ? g * kRowBytes : 0;
+    const int soff = max(min(g, g1 - 1), 0) * kRowBytes;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       unsigned char* dst = smem + buf * kTileBytes + (32 * wave + 4 * j) * kRowBytes;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rx, (__attribute__((address_space(3))) void*)(dst), 16,
-          static_cast<int>(a_voff[j] + skip), __builtin_amdgcn_readfirstlane(soff), 0, 0);
+          static_cast<int>(a_voff[j]), __builtin_amdgcn_readfirstlane(soff), 0, 0);
     }
   };
 
@@ -137,14 +136,12 @@ __global__ void __launch_bounds__(256 * KS) gemm_wide_kernel(WideArgs a) {
     uint32_t s[WN], z[WN];
   };
   auto load_b = [&](BRegs& b, int g) {
-    const bool live = g < g1;
-    const uint32_t skip = live ? 0u : kNoLoad;
-    const uint32_t gg = live ? static_cast<uint32_t>(g) : 0u;
+    const uint32_t gg = static_cast<uint32_t>(max(min(g, g1 - 1), 0));
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
-      b.c[j] = buf_load16(rp, lane_code + skip, code_off[j] + gg * kUnitBytes);
-      b.s[j] = buf_load2(rp, lane_scale + skip, scale_off[j] + gg * sbytes);
-      if (ASYM) b.z[j] = buf_load4(rp, lane_zero + skip, zero_off[j] + gg * zbytes);
+      b.c[j] = buf_load16(rp, lane_code, code_off[j] + gg * kUnitBytes);
+      b.s[j] = buf_load2(rp, lane_scale, scale_off[j] + gg * sbytes);
+      if (ASYM) b.z[j] = buf_load4(rp, lane_zero, zero_off[j] + gg * zbytes);
     }
   };
 
