@@ -83,8 +83,26 @@ struct XPass {
 // EXACT (groups of 32 or 64 channels, several scale sets per unit): the weights are
 // dequantized exactly to W_d before the matrix core, which then sums across groups; the
 // per-group correction needs one scale per matrix-core sum and does not apply.
+// The arguments are scalars rather than one struct, fourteen dwords in all, so that the
+// compiler marks them for kernarg preloading: the command processor writes them into
+// SGPRs when it launches a wavefront, and the kernel starts without waiting for a load
+// of its argument block (0.3-0.4 us of a 4-7 us decode launch on MI355X).
 template <int M, int WAVES, int BATCH, bool ASYM, bool EXACT>
-__global__ void __launch_bounds__(WAVES * 64) gemv_kernel(MvArgs a) {
+__global__ void __launch_bounds__(WAVES * 64)
+    gemv_kernel(const uint16_t* x, const uint16_t* inv, const uint8_t* packed, uint16_t* y,
+                uint32_t scales_off, uint32_t zeros_off, int N, int K, int phase_groups, int n_sets) {
+  MvArgs a;
+  a.x = x;
+  a.inv = inv;
+  a.packed = packed;
+  a.y = y;
+  a.scales_off = scales_off;
+  a.zeros_off = zeros_off;
+  a.N = N;
+  a.K = K;
+  a.n_groups = K / kGroup;
+  a.phase_groups = phase_groups;
+  a.sets = n_sets;
   constexpr int JM = M < 4 ? M : 4;  // D rows per lane that can be real rows
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int t = blockIdx.x;
@@ -294,7 +312,9 @@ hipError_t launch_fmt(const MvArgs& a, int64_t n_tiles, hipStream_t st) {
       kLdsAlone + 4 * WAVES * M * kTileN, lds_done);
   if (ea != hipSuccess) return ea;
   hipLaunchKernelGGL((gemv_kernel<M, WAVES, BATCH, ASYM, EXACT>), dim3(static_cast<unsigned>(n_tiles)),
-                     dim3(WAVES * 64), lds, st, a);
+                     dim3(WAVES * 64), lds, st, a.x, a.inv, a.packed, a.y,
+                     static_cast<uint32_t>(a.scales_off), static_cast<uint32_t>(ASYM ? a.zeros_off : 0),
+                     a.N, a.K, a.phase_groups, a.sets);
   return hipGetLastError();
 }
 
