@@ -41,13 +41,14 @@ def hipcc() -> str:
 
 
 # Matrix-core kernels keep their float32 accumulators in ordinary VGPRs: with AGPRs the
-# register allocator copies accumulators between AGPRs inside the main loop. The decode
-# kernel's scalar arguments are preloaded into SGPRs at wavefront launch (up to 16 user
-# SGPRs: the kernarg pointer and 14 argument dwords).
+# register allocator copies accumulators between AGPRs inside the main loop. Kernels
+# whose arguments are scalars (decode, narrow GEMM, split-K reduction, X' pre-scale)
+# get them preloaded into SGPRs at wavefront launch (up to 16 user SGPRs: the kernarg
+# pointer and 14 argument dwords).
 FILE_FLAGS = {
-    "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=16"],
     "gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=16"],
-    "gemm_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gemm_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=16"],
 }
 
 

@@ -30,15 +30,17 @@ struct PackedLayout {
   int64_t total_bytes;
 };
 
-inline PackedLayout make_layout(int64_t N, int64_t K, int32_t group, int32_t fmt) {
+// the layout of an N x K layer with `sets` scale / zero sets per unit; kernels whose
+// arguments are kept few call it on the device
+__host__ __device__ inline PackedLayout make_layout_sets(int64_t N, int64_t K, int64_t sets, bool asym) {
   PackedLayout L;
   L.n_tiles = (N + kTileN - 1) / kTileN;
   L.n_groups = K / kGroup;
-  L.sets = group < kGroup ? kGroup / group : 1;
+  L.sets = sets;
   L.codes_off = 0;
   L.scales_off = L.n_tiles * L.n_groups * kUnitBytes;
   int64_t end = L.scales_off + L.n_tiles * L.n_groups * L.sets * kTileN * 2;
-  if (fmt == 0) {
+  if (asym) {
     L.zeros_off = (end + 255) / 256 * 256;
     end = L.zeros_off + L.n_tiles * L.n_groups * L.sets * (kTileN / 2);
   } else {
@@ -46,6 +48,10 @@ inline PackedLayout make_layout(int64_t N, int64_t K, int32_t group, int32_t fmt
   }
   L.total_bytes = (end + 255) / 256 * 256;
   return L;
+}
+
+inline PackedLayout make_layout(int64_t N, int64_t K, int32_t group, int32_t fmt) {
+  return make_layout_sets(N, K, group < kGroup ? kGroup / group : 1, fmt == 0);
 }
 
 // the scale / zero set lane (r, p) of a unit uses: p * S / 4 for S sets per unit

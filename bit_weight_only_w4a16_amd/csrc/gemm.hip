@@ -54,10 +54,35 @@ struct GemmArgs {
 // SCHED > 0: ask the scheduler to issue each matrix instruction followed by SCHED VALU
 // instructions (and an LDS read every WN of them), so that the dequantization of the
 // next weight fragments runs while the matrix core is busy.
+// The arguments are thirteen scalar dwords (the rest of the layout is derived from
+// them), which the compiler preloads into SGPRs at wavefront launch: no wait for the
+// argument block before the first load. `out` is y (binary16) or, with K split, the
+// float32 partial sums.
 template <int WAVES_M, int WM, int WN, int SCHED, bool ASYM>
-__global__ void __launch_bounds__(kGThreads) gemm_kernel(GemmArgs a) {
+__global__ void __launch_bounds__(kGThreads)
+    gemm_kernel(const uint16_t* x, const uint16_t* inv, const uint8_t* packed, void* out, int M,
+                int N, int K, int splits, int sets) {
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int BM = WAVES_M * WM * 16, BN = WAVES_N * WN * 16;
+  const PackedLayout L = make_layout_sets(N, K, sets, ASYM);
+  GemmArgs a;
+  a.x = x;
+  a.inv = inv;
+  a.packed = packed;
+  a.y = splits > 1 ? nullptr : static_cast<uint16_t*>(out);
+  a.part = splits > 1 ? static_cast<float*>(out) : nullptr;
+  a.scales_off = L.scales_off;
+  a.zeros_off = L.zeros_off;
+  a.packed_bytes = static_cast<uint32_t>(L.total_bytes);
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.n_groups = static_cast<int>(L.n_groups);
+  a.n_tiles = static_cast<int>(L.n_tiles);
+  a.n_blocks_m = (M + BM - 1) / BM;
+  a.n_blocks_n = (N + BN - 1) / BN;
+  a.splits = splits;
+  a.sets = sets;
   constexpr int A_VEC = BM * (kGroup / 8) / kGThreads;  // 16-byte X' vectors per thread
   constexpr int BUF = BM * kLdsStride;                  // halfs per LDS buffer
   extern __shared__ __attribute__((aligned(16))) _Float16 xs[];  // [2][BM][kLdsStride]
@@ -293,8 +318,10 @@ hipError_t launch_tiles_fmt(GemmArgs a, hipStream_t st) {
   a.n_blocks_m = (a.M + BM - 1) / BM;
   a.n_blocks_n = (a.N + BN - 1) / BN;
   const unsigned blocks = static_cast<unsigned>(a.n_blocks_m) * static_cast<unsigned>(a.n_blocks_n);
+  void* out = a.splits > 1 ? static_cast<void*>(a.part) : static_cast<void*>(a.y);
   hipLaunchKernelGGL((gemm_kernel<WAVES_M, WM, WN, SCHED, ASYM>), dim3(blocks, a.splits),
-                     dim3(kGThreads), lds, st, a);
+                     dim3(kGThreads), lds, st, a.x, a.inv, a.packed, out, a.M, a.N, a.K, a.splits,
+                     a.sets);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   return launch_splitk_reduce(a.part, a.splits, static_cast<int64_t>(a.M) * a.N, a.y, st);
