@@ -210,18 +210,26 @@ def main():
     del g_all, g_one, evs
 
     # ------------------------------------------- per-kernel durations (HIP events)
-    # One graph per layer shape holding that layer's GEMV over all its weight copies,
-    # replayed between two events on the capture stream: launches run back to back, and
-    # the average per launch is the kernel time (checked against rocprofv3's trace).
+    # One graph per layer shape holding that layer's GEMV over its own set of weight
+    # copies (more than `rotate_bytes` of them, like the step, so that no launch finds its
+    # weights in the 256 MB Infinity Cache), replayed between two events on the capture
+    # stream: launches run back to back, and the average per launch is the kernel time
+    # (checked against rocprofv3's trace).
+    del copies
+    torch.cuda.empty_cache()
     per_layer = {}
     for shape_layer in ("q", "gate", "down"):
         j = next(i for i, L in enumerate(layers) if L["name"] == shape_layer)
         L = layers[j]
-        reps = max(2, (8 * K) // (7 * rot))
-        us = graph_us([product(awq.awq_gemv, L, copies[j][r], ws) for r in range(rot)], reps)
+        lrot = rotation(L["packed"].numel())
+        lcp = [L["packed"]] + [L["packed"].clone() for _ in range(lrot - 1)]
+        reps = max(2, (8 * K) // (7 * lrot))
+        us = graph_us([product(awq.awq_gemv, L, lcp[r], ws) for r in range(lrot)], reps)
         per_layer[shape_layer] = {"shape": f"{L['k']}->{L['n']}", "us": round(us, 3),
                                   "GB/s": round(L["bytes"] / us / 1e3, 1),
-                                  "launches": 3 * reps * rot}
+                                  "launches": 3 * reps * lrot, "weight_copies": lrot}
+        del lcp
+        torch.cuda.empty_cache()
     # The dominant kernel is the decode kernel itself: its 7 launches are the whole step
     # (the 4096 -> 4096 launches alone are 45 % of it). Roofline over one step: the
     # algorithmic bytes of the 7 launches / their summed kernel time, i.e. bytes per
@@ -229,7 +237,7 @@ def main():
     sum_kernel_us = 4 * per_layer["q"]["us"] + 2 * per_layer["gate"]["us"] + per_layer["down"]["us"]
     achieved = step_bytes / sum_kernel_us / 1e3  # GB/s
     traffic = measured_traffic()
-    del copies, layers
+    del layers
     torch.cuda.empty_cache()
 
     extra = {}

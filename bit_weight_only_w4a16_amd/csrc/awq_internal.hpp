@@ -130,6 +130,16 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
                                               __builtin_amdgcn_readfirstlane(static_cast<int>(soff)), 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+// The same 16-byte load marked non-temporal (the `nt` cache-policy bit): for data read
+// exactly once per call, so the caches keep the lines that are reused instead.
+__device__ __forceinline__ uint4 buf_load16_stream(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+  constexpr int kNonTemporal = 2;
+  const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff),
+                                              __builtin_amdgcn_readfirstlane(static_cast<int>(soff)),
+                                              kNonTemporal);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(voff),
                                               __builtin_amdgcn_readfirstlane(static_cast<int>(soff)), 0);
