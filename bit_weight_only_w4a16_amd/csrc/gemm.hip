@@ -356,12 +356,22 @@ hipError_t launch_splitk_reduce(const float* part, int splits, int64_t mn, uint1
   return hipGetLastError();
 }
 
+// Up to 16 rows on a layer of at most 256 row tiles, the decode kernel (one workgroup per
+// tile and all of K: no split, no second launch, no workspace) is faster than the split-K
+// tiles, as long as the staged activations of its groups fit in LDS in about one pass
+// (measured on MI355X: 4096 -> 4096 at M = 8, 5.3 instead of 8.2 us; 11008 -> 4096 at
+// M = 8, 11.4 instead of 12.7 us; at M = 12 on that layer it is slower).
+static bool small_m_takes_decode_kernel(int64_t M, int64_t N, int64_t K) {
+  return M <= 16 && (N + kTileN - 1) / kTileN <= 256 && M * (K / kGroup) <= 704;
+}
+
 // Large M runs the wide-tile kernel, which needs X' in the workspace when inv_s_c is
 // given.
 constexpr int64_t kWideMinM = 256;
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M >= kWideMinM) return gemm_wide_workspace_bytes(M, N, K);
+  if (small_m_takes_decode_kernel(M, N, K)) return 0;
   const int s = pick_splits(default_blocks(M, N, K), M, N, K, static_cast<int>(K / kGroup));
   return s > 1 ? static_cast<size_t>(s) * M * N * sizeof(float) : 0;
 }
@@ -380,6 +390,9 @@ hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* p
     return launch_gemm_wide(x, inv_s_c, packed, M, N, K, group, fmt, y, ws, ws_bytes, cfg, st);
   }
   const PackedLayout L = make_layout(N, K, group, fmt);
+  if (small_m_takes_decode_kernel(M, N, K)) {
+    return launch_gemv(x, inv_s_c, packed, M, N, K, group, fmt, y, nullptr, 0, st);
+  }
   GemmArgs a;
   a.x = x;
   a.inv = inv_s_c;

@@ -60,8 +60,12 @@ def test_sizes():
     assert awq.awq_repacked_bytes(64, 256, 256) == awq.awq_repacked_bytes(64, 256, 128)
     assert awq.awq_workspace_bytes(0, 4096, 4096) == 0
     # split-K partial sums only where the output blocks alone leave CUs idle
-    assert awq.awq_workspace_bytes(16, 4096, 4096) % (16 * 4096 * 4) == 0
-    assert awq.awq_workspace_bytes(16, 4096, 4096) > 0
+    assert awq.awq_workspace_bytes(16, 11008, 4096) % (16 * 11008 * 4) == 0
+    assert awq.awq_workspace_bytes(16, 11008, 4096) > 0
+    # up to 16 rows on at most 256 row tiles the decode kernel runs: no workspace
+    assert awq.awq_workspace_bytes(16, 4096, 4096) == 0
+    assert awq.awq_workspace_bytes(8, 4096, 11008) == 0
+    assert awq.awq_workspace_bytes(12, 4096, 11008) > 0
     # large M: X' = X * inv_s_c formed once, M x K binary16
     assert awq.awq_workspace_bytes(2048, 4096, 4096) == 2048 * 4096 * 2
     # M >= 256 with few output blocks: X' (256-byte aligned) then float32 sums of the

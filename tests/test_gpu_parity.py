@@ -254,6 +254,20 @@ def test_gemm_parity(n, k, m, fmt):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("n,k,m", [(4104, 512, 7), (4112, 1024, 16), (4120, 256, 1), (4096, 12288, 9)])
+def test_gemm_parity_split_tiles_small_m(n, k, m, fmt):
+    """Up to 16 rows on more than 256 row tiles (or long rows), awq_gemm runs its own
+    narrow tiles with K split across workgroups (the smaller layers go to the decode
+    kernel); unsplit without a workspace."""
+    d, g, o, y_ref = product_case(n, k, m, fmt)
+    x = to_dev(d["x"])
+    ws = awq.workspace(m, n, k, DEV)
+    for w in (ws, None):
+        y = awq.awq_gemm(x, g["inv"], g["packed"], n, k, 128, fmt, ws=w)
+        assert rel_err(y.cpu().numpy(), y_ref) <= TOL
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("n,k,m", [(512, 4096, 256), (520, 8192, 300)])
 def test_wide_gemm_split_k(n, k, m, fmt):
     """M >= 256 with too few 128 x 256 output blocks for the CUs: K is split across
