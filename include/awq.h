@@ -158,9 +158,10 @@ int awq_dequant(const void* w, const uint16_t* scales, const int32_t* qzeros,
 /*
  * Workspace bytes for an M x N x K call of awq_gemv / awq_gemm (0: none used).
  * awq_gemv keeps every partial sum inside a workgroup and uses none. awq_gemm uses it
- *  - at small M, when its output blocks alone would leave CUs idle: K is split across
- *    workgroups, the float32 partial sums [splits][M][N] go to the workspace and a
- *    second kernel adds them in split order;
+ *  - at small M, when its output blocks alone would leave CUs idle (and the call does
+ *    not run the awq_gemv kernel, see awq_gemm): K is split across workgroups, the
+ *    float32 partial sums [splits][M][N] go to the workspace and a second kernel adds
+ *    them in split order;
  *  - at M >= 256 with inv_s_c given: X' = binary16(X * inv_s_c) is formed once into the
  *    workspace ([M][K] binary16) and the wide-tile kernel streams it into LDS;
  *  - at M >= 256 when the 128 x 256 output blocks cover fewer than half of the CUs: K is
@@ -201,9 +202,11 @@ int awq_gemv(const uint16_t* x, const uint16_t* inv_s_c, const void* packed, int
  * batches turn the product into a matrix-matrix multiply; section "Kernel Execution:
  * Marlin vs. ExLlamaV2 INT4 GEMM Micro-Architecture": weights are unpacked to
  * binary16 just before the matrix instruction). Same arguments, math and accuracy as
- * awq_gemv; the dequantized weights fed to the matrix cores are exactly W_d. The
- * split of K (see awq_workspace_bytes) depends only on M, N, K and whether a large
- * enough workspace is given, so repeated calls give the same bits.
+ * awq_gemv; the dequantized weights fed to the matrix cores are exactly W_d. Up to 16
+ * rows on a layer of at most 256 row tiles (N <= 4096) with M * K / 128 <= 704, it runs
+ * the awq_gemv kernel instead (faster there: no split of K, no second launch). Which
+ * kernel runs and the split of K (see awq_workspace_bytes) depend only on M, N, K and
+ * whether a large enough workspace is given, so repeated calls give the same bits.
  * Errors: INVALID_ARG, UNSUPPORTED, MISALIGNED, WORKSPACE, HIP.
  */
 int awq_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* packed, int64_t M,
