@@ -241,7 +241,7 @@ def test_gemv_parity_long_rows(n, k, m, fmt):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
-@pytest.mark.parametrize("m", [1, 7, 16, 33, 64, 130, 256, 300])
+@pytest.mark.parametrize("m", [1, 7, 16, 20, 32, 33, 64, 130, 256, 300])
 @pytest.mark.parametrize("n,k", [(512, 512), (200, 1024), (72, 256), (200, 2048)])
 def test_gemm_parity(n, k, m, fmt):
     d, g, o, y_ref = product_case(n, k, m, fmt)
@@ -350,6 +350,8 @@ FULL = [
     ("70b_up_sym_m1", 28672, 8192, 1, 1, "gemv"),
     ("70b_down_asym_m1", 8192, 28672, 1, 0, "gemv"),
     ("70b_up_asym_m16_gemv", 28672, 8192, 16, 0, "gemv"),
+    ("70b_up_asym_m32", 28672, 8192, 32, 0, "gemm"),
+    ("70b_down_sym_m24", 8192, 28672, 24, 1, "gemm"),
     ("7b_down_m8_gemv", 4096, 11008, 8, 0, "gemv"),
     ("7b_down_m16_gemv", 4096, 11008, 16, 0, "gemv"),
     ("70b_down_sym_m16", 8192, 28672, 16, 1, "gemm"),
