@@ -338,6 +338,7 @@ int64_t default_blocks(int64_t M, int64_t N, int64_t K) {
   if (M <= 16) return blocks_of<1, 1, 2>(M, N);
   if (M <= 32 && N * K <= (int64_t{1} << 26)) return blocks_of<1, 2, 1>(M, N);
   if (M <= 32) return blocks_of<1, 2, 2>(M, N);
+  if (M <= 64 && N * K <= (int64_t{1} << 26)) return blocks_of<1, 2, 2>(M, N);
   if (M <= 64) return blocks_of<1, 4, 2>(M, N);
   if (K >= 8192 || N >= 16384) return blocks_of<1, 8, 2>(M, N);
   return blocks_of<1, 4, 4>(M, N);
@@ -450,7 +451,8 @@ hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* p
   // weights, and narrow workgroup tiles give the most workgroups (16 x 64 up to M = 16 for
   // layers of at most 2^26 weights, else 16 x 128; 32 x 64 / 32 x 128 up to M = 32, where
   // each dequantized weight fragment serves both row tiles: 10-20 % faster than two
-  // 16-row blocks; 64 x 128 up to M = 64), K split so that
+  // 16-row blocks; up to M = 64, 32 x 128 on layers of at most 2^26 weights (more
+  // workgroups than 64 x 128: 5-22 % faster there), else 64 x 128), K split so that
   // the workgroups cover the CUs about 2.5 times; at larger M a 64 x 256 tile (each wavefront
   // 64 x 64) runs best, or for long K or wide N a 128 x 128 tile (each wavefront 128 x
   // 32), which dequantizes each weight fragment for 8 row tiles.
@@ -458,6 +460,7 @@ hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* p
   if (M <= 16) return launch_tiles<1, 1, 2>(a, st);
   if (M <= 32 && N * K <= (int64_t{1} << 26)) return launch_tiles<1, 2, 1>(a, st);
   if (M <= 32) return launch_tiles<1, 2, 2>(a, st);
+  if (M <= 64 && N * K <= (int64_t{1} << 26)) return launch_tiles<1, 2, 2>(a, st);
   if (M <= 64) return launch_tiles<1, 4, 2>(a, st);
   if (K >= 8192 || N >= 16384) return launch_tiles<1, 8, 2>(a, st);
   return launch_tiles<1, 4, 4>(a, st);
