@@ -382,14 +382,18 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
                        int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt, uint16_t* y,
                        void* ws, size_t ws_bytes, hipStream_t st) {
-  // large M: wide wavefront tiles, X' from the workspace (or pre-scaled by the caller);
-  // AWQ_GEMM_WIDE = "0" keeps the narrow kernel, "[splits]<column tiles><K split>" (41,
-  // 42, 31, 32, 21, 22, 442, ...) forces a wide configuration (for tuning sweeps)
-  const char* wide = getenv("AWQ_GEMM_WIDE");
+  // large M: wide wavefront tiles, X' from the workspace (or pre-scaled by the caller).
+  // Tuning overrides for sweeps, read once per process: AWQ_GEMM_WIDE = "0" keeps the
+  // narrow kernel, "[splits]<column tiles><K split>" (41, 42, 31, 32, 21, 22, 442, ...)
+  // forces a wide configuration.
+  static const int wide_env = [] {
+    const char* w = getenv("AWQ_GEMM_WIDE");
+    return w == nullptr ? -1 : (w[0] == '0' ? 0 : atoi(w));
+  }();
   const bool wide_ok =
       inv_s_c == nullptr || (ws != nullptr && ws_bytes >= static_cast<size_t>(M) * K * 2);
-  if (M >= kWideMinM && wide_ok && !(wide && wide[0] == '0')) {
-    const int cfg = wide ? atoi(wide) : 0;
+  if (M >= kWideMinM && wide_ok && wide_env != 0) {
+    const int cfg = wide_env > 0 ? wide_env : 0;
     return launch_gemm_wide(x, inv_s_c, packed, M, N, K, group, fmt, y, ws, ws_bytes, cfg, st);
   }
   const PackedLayout L = make_layout(N, K, group, fmt);
@@ -415,20 +419,31 @@ hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* p
   a.splits = 1;
   a.part = nullptr;
   int want = pick_splits(default_blocks(M, N, K), M, N, K, a.n_groups);
-  // AWQ_GEMM_SPLITS = "<splits>" forces the K split (for tuning sweeps; needs a workspace
-  // of splits * M * N * 4 bytes, else the product runs unsplit)
-  if (const char* sp = getenv("AWQ_GEMM_SPLITS")) {
-    const int v = atoi(sp);
-    if (v >= 1 && v <= 16 && v <= a.n_groups) want = v;
-  }
+  // AWQ_GEMM_SPLITS = "<splits>" forces the K split (tuning sweeps, read once; needs a
+  // workspace of splits * M * N * 4 bytes, else the product runs unsplit)
+  static const int splits_env = [] {
+    const char* sp = getenv("AWQ_GEMM_SPLITS");
+    return sp == nullptr ? 0 : atoi(sp);
+  }();
+  if (splits_env >= 1 && splits_env <= 16 && splits_env <= a.n_groups) want = splits_env;
   if (want > 1 && ws != nullptr && ws_bytes >= static_cast<size_t>(want) * M * N * sizeof(float)) {
     a.splits = want;
     a.part = static_cast<float*>(ws);
   }
-  // AWQ_GEMM_TILE = "waves_m,wm,wn,sched" selects another tiling (for tuning sweeps)
-  const char* env = getenv("AWQ_GEMM_TILE");
-  int wv = 0, wm = 0, wn = 0, sc = 0;
-  if (env && sscanf(env, "%d,%d,%d,%d", &wv, &wm, &wn, &sc) == 4) {
+  // AWQ_GEMM_TILE = "waves_m,wm,wn,sched" selects another tiling (tuning sweeps, read
+  // once)
+  struct TileEnv {
+    int wv = 0, wm = 0, wn = 0, sc = 0;
+    bool set = false;
+  };
+  static const TileEnv tile_env = [] {
+    TileEnv t;
+    const char* env = getenv("AWQ_GEMM_TILE");
+    t.set = env != nullptr && sscanf(env, "%d,%d,%d,%d", &t.wv, &t.wm, &t.wn, &t.sc) == 4;
+    return t;
+  }();
+  if (tile_env.set) {
+    const int wv = tile_env.wv, wm = tile_env.wm, wn = tile_env.wn, sc = tile_env.sc;
     if (wv == 1 && wm == 4 && wn == 4 && sc == 0) return launch_tiles<1, 4, 4, 0>(a, st);
     if (wv == 1 && wm == 4 && wn == 4 && sc == 2) return launch_tiles<1, 4, 4, 2>(a, st);
     if (wv == 1 && wm == 4 && wn == 4 && sc == 3) return launch_tiles<1, 4, 4, 3>(a, st);

@@ -351,20 +351,22 @@ hipError_t launch_m(const MvArgs& a, int64_t n_tiles, hipStream_t st) {
   return launch_cfg<M, 8, 1>(a, n_tiles, st);
 }
 
-// Tuning override for sweeps (M = 1 only): AWQ_GEMV_CFG = "waves,batch".
+// Tuning override for sweeps (M = 1 only), read once per process:
+// AWQ_GEMV_CFG = "waves,batch".
 hipError_t launch_m1(const MvArgs& a, int64_t n_tiles, hipStream_t st) {
-  const char* env = getenv("AWQ_GEMV_CFG");
-  if (env) {
+  static const int cfg = [] {
+    const char* env = getenv("AWQ_GEMV_CFG");
     int w = 0, b = 0;
-    if (sscanf(env, "%d,%d", &w, &b) == 2) {
-      if (w == 4 && b == 2) return launch_cfg<1, 4, 2>(a, n_tiles, st);
-      if (w == 8 && b == 1) return launch_cfg<1, 8, 1>(a, n_tiles, st);
-      if (w == 8 && b == 2) return launch_cfg<1, 8, 2>(a, n_tiles, st);
-      if (w == 16 && b == 1) return launch_cfg<1, 16, 1>(a, n_tiles, st);
-      if (w == 16 && b == 2) return launch_cfg<1, 16, 2>(a, n_tiles, st);
-    }
+    return env != nullptr && sscanf(env, "%d,%d", &w, &b) == 2 ? 10 * w + b : 0;
+  }();
+  switch (cfg) {
+    case 42: return launch_cfg<1, 4, 2>(a, n_tiles, st);
+    case 81: return launch_cfg<1, 8, 1>(a, n_tiles, st);
+    case 82: return launch_cfg<1, 8, 2>(a, n_tiles, st);
+    case 161: return launch_cfg<1, 16, 1>(a, n_tiles, st);
+    case 162: return launch_cfg<1, 16, 2>(a, n_tiles, st);
+    default: return launch_m<1>(a, n_tiles, st);
   }
-  return launch_m<1>(a, n_tiles, st);
 }
 
 }  // namespace
