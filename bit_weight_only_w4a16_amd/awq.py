@@ -288,11 +288,12 @@ class QuantLinear:
 
     Built from fp16 weights with ``QuantLinear.from_weight`` (channel scale from
     calibration rows, fold, quantize, pack, repack -- all in the library's kernels).
-    Calls go to awq_gemv for M <= gemv_max_m rows and to awq_gemm above (on MI355X the
-    split-K GEMM overtakes the decode kernel between 4 and 8 rows).
+    Calls go to awq_gemm, which runs the decode kernel itself where that is faster (a few
+    rows, or up to 16 rows on small layers); ``gemv_max_m`` sends up to that many rows to
+    awq_gemv directly instead.
     """
 
-    def __init__(self, packed, n, k, inv_s_c=None, group=GROUP, fmt=FMT_ASYM, gemv_max_m=4):
+    def __init__(self, packed, n, k, inv_s_c=None, group=GROUP, fmt=FMT_ASYM, gemv_max_m=0):
         self.packed, self.n, self.k = packed, n, k
         self.inv_s_c, self.group, self.fmt = inv_s_c, group, fmt
         self.gemv_max_m = gemv_max_m

@@ -359,13 +359,19 @@ hipError_t launch_splitk_reduce(const float* part, int splits, int64_t mn, uint1
   return hipGetLastError();
 }
 
-// Up to 16 rows on a layer of at most 256 row tiles, the decode kernel (one workgroup per
-// tile and all of K: no split, no second launch, no workspace) is faster than the split-K
-// tiles, as long as the staged activations of its groups fit in LDS in about one pass
-// (measured on MI355X: 4096 -> 4096 at M = 8, 5.3 instead of 8.2 us; 11008 -> 4096 at
-// M = 8, 11.4 instead of 12.7 us; at M = 12 on that layer it is slower).
+// Where the decode kernel (one workgroup per 16-row tile and all of K: no split, no second
+// launch, no workspace) is faster than the split-K tiles (measured on MI355X, 4096 <= K, N
+// <= 28672): always at M <= 2 (4096 -> 11008: 6.5 / 7.3 instead of 10.2 / 10.4 us; the
+// 70B layers: 21.6 / 24.3 instead of 28.0 / 27.8 us); at M <= 4 on layers of at most 2^15
+// 16 x 128 units (4096 -> 11008 at M = 4: 9.4 instead of 10.6 us; on the 70B layers it is
+// slower); and up to 16 rows on layers of at most 256 row tiles while the staged
+// activations of its groups fit in LDS in about one pass (4096 -> 4096 at M = 8, 5.3
+// instead of 8.2 us; 11008 -> 4096 at M = 8, 11.4 instead of 12.7 us).
 static bool small_m_takes_decode_kernel(int64_t M, int64_t N, int64_t K) {
-  return M <= 16 && (N + kTileN - 1) / kTileN <= 256 && M * (K / kGroup) <= 704;
+  const int64_t tiles = (N + kTileN - 1) / kTileN, groups = K / kGroup;
+  if (M <= 2) return true;
+  if (M <= 4 && tiles * groups <= (int64_t{1} << 15)) return true;
+  return M <= 16 && tiles <= 256 && M * groups <= 704;
 }
 
 // Large M runs the wide-tile kernel, which needs X' in the workspace when inv_s_c is

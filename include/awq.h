@@ -202,9 +202,10 @@ int awq_gemv(const uint16_t* x, const uint16_t* inv_s_c, const void* packed, int
  * batches turn the product into a matrix-matrix multiply; section "Kernel Execution:
  * Marlin vs. ExLlamaV2 INT4 GEMM Micro-Architecture": weights are unpacked to
  * binary16 just before the matrix instruction). Same arguments, math and accuracy as
- * awq_gemv; the dequantized weights fed to the matrix cores are exactly W_d. Up to 16
- * rows on a layer of at most 256 row tiles (N <= 4096) with M * K / 128 <= 704, it runs
- * the awq_gemv kernel instead (faster there: no split of K, no second launch). Which
+ * awq_gemv; the dequantized weights fed to the matrix cores are exactly W_d. It runs
+ * the awq_gemv kernel instead where that is faster (no split of K, no second launch):
+ * at M <= 2; at M <= 4 when ceil(N / 16) * K / 128 <= 32768; and up to 16 rows when
+ * ceil(N / 16) <= 256 and M * K / 128 <= 704. Which
  * kernel runs and the split of K (see awq_workspace_bytes) depend only on M, N, K and
  * whether a large enough workspace is given, so repeated calls give the same bits.
  * Errors: INVALID_ARG, UNSUPPORTED, MISALIGNED, WORKSPACE, HIP.

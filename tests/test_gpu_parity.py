@@ -298,6 +298,22 @@ def test_products_with_prescaled_activations(m):
             assert rel_err(y.cpu().numpy(), y_ref) <= TOL
 
 
+@pytest.mark.parametrize("m", [1, 3, 20])
+def test_quant_linear_wrapper(m):
+    """QuantLinear.from_weight builds the layer with the library's kernels (channel scale,
+    fold, pack, repack) and its calls agree with the oracle's product."""
+    n, k = 264, 1024
+    d = synth.layer_inputs(2, m, n, k)
+    layer = awq.QuantLinear.from_weight(to_dev(d["w"]), to_dev(d["x_cal"]))
+    o = oracle_quantize(d["w"], d["x_cal"], 0)
+    y_ref = oracle.matmul_ref(d["x"], o["w_d"], o["inv"])
+    y = layer(to_dev(d["x"]))
+    assert y.shape == (m, n)
+    assert rel_err(y.cpu().numpy(), y_ref) <= TOL
+    y2 = awq.QuantLinear(layer.packed, n, k, layer.inv_s_c, gemv_max_m=16)(to_dev(d["x"]))
+    assert rel_err(y2.cpu().numpy(), y_ref) <= TOL
+
+
 def test_zero_weights_give_zero_output():
     n, k = 128, 512
     w = np.zeros((n, k), dtype=np.float16)
