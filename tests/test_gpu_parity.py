@@ -254,7 +254,7 @@ def test_gemm_parity(n, k, m, fmt):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
-@pytest.mark.parametrize("n,k,m", [(4104, 512, 7), (4112, 1024, 16), (4120, 256, 1), (4096, 12288, 9)])
+@pytest.mark.parametrize("n,k,m", [(4104, 512, 7), (4112, 1024, 16), (4120, 256, 5), (4096, 12288, 9)])
 def test_gemm_parity_split_tiles_small_m(n, k, m, fmt):
     """Up to 16 rows on more than 256 row tiles (or long rows), awq_gemm runs its own
     narrow tiles with K split across workgroups (the smaller layers go to the decode
@@ -367,6 +367,7 @@ FULL = [
     ("70b_down_asym_m1", 8192, 28672, 1, 0, "gemv"),
     ("70b_up_asym_m16_gemv", 28672, 8192, 16, 0, "gemv"),
     ("70b_up_asym_m32", 28672, 8192, 32, 0, "gemm"),
+    ("70b_down_asym_m3", 8192, 28672, 3, 0, "gemm"),
     ("70b_down_sym_m24", 8192, 28672, 24, 1, "gemm"),
     ("7b_down_m8_gemv", 4096, 11008, 8, 0, "gemv"),
     ("7b_down_m16_gemv", 4096, 11008, 16, 0, "gemv"),
