@@ -284,10 +284,11 @@ def test_wide_gemm_split_k(n, k, m, fmt):
     assert rel_err(y1.cpu().numpy(), y_ref) <= TOL
 
 
-@pytest.mark.parametrize("m", [3, 300])
-def test_products_with_prescaled_activations(m):
-    """inv_s_c NULL: the caller passes X' = X * inv_s_c already in binary16."""
-    n, k = 256, 1024
+@pytest.mark.parametrize("m,k", [(3, 1024), (300, 1024), (40, 1024), (40, 4096)])
+def test_products_with_prescaled_activations(m, k):
+    """inv_s_c NULL: the caller passes X' = X * inv_s_c already in binary16 (decode
+    kernel, wide tiles, narrow tiles unsplit and with K split over four workgroups)."""
+    n = 256
     d, g, o, _ = product_case(n, k, m, 0)
     xs = oracle.fp16_rn(oracle.as_f64(d["x"]) * o["inv"][None, :]).astype(np.float16)
     y_ref = oracle.matmul_ref(xs, o["w_d"])
@@ -453,6 +454,27 @@ def test_group_sizes(n, k, group, fmt):
     y = awq.awq_gemm(to_dev(xl), g["inv"], g["packed"], n, k, g_size, fmt,
                      ws=awq.workspace(300, n, k, DEV, g_size))
     assert rel_err(y.cpu().numpy(), y_ref) <= TOL
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("group", [32, 64, 256, "K"])
+def test_group_sizes_split_k_tiles(group, fmt):
+    """The narrow matrix-core tiles with K split over four workgroups (M = 20: 32 x 64
+    blocks, M = 40: 32 x 128 blocks; 264 rows, so the last block is ragged) with
+    several scale sets per packed unit (G = 32, 64) or one repeated set (G = 256, per
+    channel): each lane must take the scale and zero of its own channels' group."""
+    n, k = 264, 4096
+    g_size = k if group == "K" else group
+    d = synth.layer_inputs(13, 40, n, k)
+    g = gpu_quantize(d["w"], d["x_cal"], fmt, group=g_size)
+    o = oracle_quantize(d["w"], d["x_cal"], fmt, group=g_size)
+    for m in (20, 40):
+        assert awq.awq_workspace_bytes(m, n, k, g_size) == 4 * m * n * 4   # four K splits
+        x = d["x"][:m]
+        y_ref = oracle.matmul_ref(x, o["w_d"], o["inv"])
+        y = awq.awq_gemm(to_dev(x), g["inv"], g["packed"], n, k, g_size, fmt,
+                         ws=awq.workspace(m, n, k, DEV, g_size))
+        assert rel_err(y.cpu().numpy(), y_ref) <= TOL
 
 
 @pytest.mark.parametrize("group", [32, 64, "K"])
