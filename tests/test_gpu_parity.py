@@ -284,7 +284,7 @@ def test_wide_gemm_split_k(n, k, m, fmt):
     assert rel_err(y1.cpu().numpy(), y_ref) <= TOL
 
 
-@pytest.mark.parametrize("m,k", [(3, 1024), (300, 1024), (40, 1024), (40, 4096)])
+@pytest.mark.parametrize("m,k", [(3, 1024), (12, 1024), (300, 1024), (40, 1024), (40, 4096)])
 def test_products_with_prescaled_activations(m, k):
     """inv_s_c NULL: the caller passes X' = X * inv_s_c already in binary16 (decode
     kernel, wide tiles, narrow tiles unsplit and with K split over four workgroups)."""
@@ -474,6 +474,23 @@ def test_group_sizes_split_k_tiles(group, fmt):
         y_ref = oracle.matmul_ref(x, o["w_d"], o["inv"])
         y = awq.awq_gemm(to_dev(x), g["inv"], g["packed"], n, k, g_size, fmt,
                          ws=awq.workspace(m, n, k, DEV, g_size))
+        assert rel_err(y.cpu().numpy(), y_ref) <= TOL
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("group", [32, 64])
+def test_group_sizes_long_rows(group, fmt):
+    """Decode on rows of 13312 channels (at M = 8 the staged activations take two LDS
+    phases) with four or two scale sets per packed unit; below 128 channels per group
+    both M take the exact-dequantization form."""
+    n, k = 64, 13312
+    d = synth.layer_inputs(17, 8, n, k)
+    g = gpu_quantize(d["w"], d["x_cal"], fmt, group=group)
+    o = oracle_quantize(d["w"], d["x_cal"], fmt, group=group)
+    for m in (1, 8):
+        x = d["x"][:m]
+        y_ref = oracle.matmul_ref(x, o["w_d"], o["inv"])
+        y = awq.awq_gemv(to_dev(x), g["inv"], g["packed"], n, k, group, fmt)
         assert rel_err(y.cpu().numpy(), y_ref) <= TOL
 
 
