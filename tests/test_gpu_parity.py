@@ -400,17 +400,18 @@ def test_full_shape_sampled(name, n, k, m, fmt, fn):
 
 # ----------------------------------------------------------------- AWQ scale search
 
-@pytest.mark.parametrize("fmt,rows", [(0, 32), (1, 32), (0, 40)])
-def test_scale_search_matches_oracle(fmt, rows):
+@pytest.mark.parametrize("fmt,rows,group", [(0, 32, 128), (1, 32, 128), (0, 40, 128),
+                                            (0, 32, 64), (1, 32, 32)])
+def test_scale_search_matches_oracle(fmt, rows, group):
     """Device grid search vs the oracle's: every loss close (the device path rounds X'
     and y to binary16, as deployed), the device's choice optimal by the oracle's measure
-    within 1 %, and the same bits on a second call."""
+    within 1 %, and the same bits on a second call; also with groups of 64 and 32."""
     n, k, grid = 256, 1024, 20
     d = synth.layer_inputs(0, rows, n, k)
     x_cal = d["x_cal"] if rows == 32 else synth.activations(rows, k, 77, d["outliers"])
-    best, losses = awq.awq_scale_search(to_dev(d["w"]), to_dev(x_cal), 128, fmt, grid)
+    best, losses = awq.awq_scale_search(to_dev(d["w"]), to_dev(x_cal), group, fmt, grid)
     torch.cuda.synchronize()
-    a_o, l_o = oracle.scale_search(d["w"], x_cal, 128, fmt, grid)
+    a_o, l_o = oracle.scale_search(d["w"], x_cal, group, fmt, grid)
     l_g = losses.cpu().numpy()
     assert np.all(np.isfinite(l_g))
     assert np.allclose(l_g, l_o, rtol=3e-2)
@@ -418,7 +419,7 @@ def test_scale_search_matches_oracle(fmt, rows):
     assert best.item() == ig / grid
     assert l_g[ig] == l_g.min() and np.argmin(l_g) == ig
     assert l_o[ig] <= l_o.min() * 1.01
-    best2, losses2 = awq.awq_scale_search(to_dev(d["w"]), to_dev(x_cal), 128, fmt, grid)
+    best2, losses2 = awq.awq_scale_search(to_dev(d["w"]), to_dev(x_cal), group, fmt, grid)
     torch.cuda.synchronize()
     assert torch.equal(losses, losses2) and torch.equal(best, best2)
 
