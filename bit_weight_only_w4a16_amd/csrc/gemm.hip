@@ -280,13 +280,20 @@ __global__ void __launch_bounds__(kGThreads)
 }
 
 // y = binary16(sum over the splits of the partial sums, in split order): deterministic.
-// Four outputs per thread; M * N is a multiple of 8.
-__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* part, int splits,
-                                                            int64_t mn, uint16_t* y) {
+// Four outputs per thread; M * N is a multiple of 8. The split count is a template
+// argument so that all S loads are in flight before the first add (with a run-time
+// count the loop waited one memory round trip per split).
+template <int S>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* part, int64_t mn,
+                                                            uint16_t* y) {
   const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
   if (i >= mn) return;
-  float4_t v = *reinterpret_cast<const float4_t*>(part + i);
-  for (int s = 1; s < splits; ++s) v += *reinterpret_cast<const float4_t*>(part + s * mn + i);
+  float4_t p[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) p[s] = *reinterpret_cast<const float4_t*>(part + s * mn + i);
+  float4_t v = p[0];
+#pragma unroll
+  for (int s = 1; s < S; ++s) v += p[s];
   const half2_t lo = {static_cast<_Float16>(v[0]), static_cast<_Float16>(v[1])};
   const half2_t hi = {static_cast<_Float16>(v[2]), static_cast<_Float16>(v[3])};
   *reinterpret_cast<uint2*>(y + i) = make_uint2(as_u32(lo), as_u32(hi));
@@ -350,13 +357,36 @@ hipError_t launch_tiles(GemmArgs a, hipStream_t st) {
   return launch_tiles_fmt<WAVES_M, WM, WN, SCHED, false>(a, st);
 }
 
+template <int S>
+hipError_t launch_reduce_s(const float* part, int64_t mn, uint16_t* y, hipStream_t st) {
+  hipLaunchKernelGGL(splitk_reduce_kernel<S>, dim3(static_cast<unsigned>((mn / 4 + 255) / 256)),
+                     dim3(256), 0, st, part, mn, y);
+  return hipGetLastError();
+}
+
 }  // namespace
 
+// splits in [2, 16] (every K split the launchers pick or accept)
 hipError_t launch_splitk_reduce(const float* part, int splits, int64_t mn, uint16_t* y,
                                 hipStream_t st) {
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(static_cast<unsigned>((mn / 4 + 255) / 256)),
-                     dim3(256), 0, st, part, splits, mn, y);
-  return hipGetLastError();
+  switch (splits) {
+    case 2: return launch_reduce_s<2>(part, mn, y, st);
+    case 3: return launch_reduce_s<3>(part, mn, y, st);
+    case 4: return launch_reduce_s<4>(part, mn, y, st);
+    case 5: return launch_reduce_s<5>(part, mn, y, st);
+    case 6: return launch_reduce_s<6>(part, mn, y, st);
+    case 7: return launch_reduce_s<7>(part, mn, y, st);
+    case 8: return launch_reduce_s<8>(part, mn, y, st);
+    case 9: return launch_reduce_s<9>(part, mn, y, st);
+    case 10: return launch_reduce_s<10>(part, mn, y, st);
+    case 11: return launch_reduce_s<11>(part, mn, y, st);
+    case 12: return launch_reduce_s<12>(part, mn, y, st);
+    case 13: return launch_reduce_s<13>(part, mn, y, st);
+    case 14: return launch_reduce_s<14>(part, mn, y, st);
+    case 15: return launch_reduce_s<15>(part, mn, y, st);
+    case 16: return launch_reduce_s<16>(part, mn, y, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // Where the decode kernel (one workgroup per 16-row tile and all of K: no split, no second

@@ -361,7 +361,7 @@ hipError_t launch_gemm_wide(const uint16_t* x, const uint16_t* inv_s_c, const vo
   a.n_tiles = static_cast<int>(L.n_tiles);
   a.sets = static_cast<int>(L.sets);
   WidePick w = pick_wide(M, N, K);
-  if (cfg != 0) w = {(cfg / 10) % 10, cfg % 10, cfg >= 100 ? cfg / 100 : 1};
+  if (cfg != 0) w = {(cfg / 10) % 10, cfg % 10, cfg >= 100 ? (cfg / 100 < 16 ? cfg / 100 : 16) : 1};
   const int64_t part_off = align256(M * K * 2);
   a.splits = 1;
   a.part = nullptr;
