@@ -367,11 +367,80 @@ def pin_layout_orientation(o):
     assert s2.shape == (2, 1) and np.array_equal(s2[:, 0], [0.5, 1.0])
 
 
+# ------------------------------------------------ objective of the scale search
+
+def _loss_case():
+    g = load_golden("awq_loss_hand.txt")
+    w = np.zeros((8, 8))
+    w[0] = _nums(g["w.row0"])
+    x = np.stack([_nums(g["x.row0"]), _nums(g["x.row1"])])
+    return g, w, x, int(g["group"])
+
+
+def pin_loss_hand_value(o):
+    """The hand-worked loss of tests/golden/awq_loss_hand.txt: 5 with s = 1 and with
+    s = 2 on every channel (asymmetric format)."""
+    g, w, x, group = _loss_case()
+    for s_val, key in ((1.0, "expect.loss_s1"), (2.0, "expect.loss_s2")):
+        loss = o.awq_loss(w, x, np.full(8, s_val), group, o.FMT_ASYM)
+        assert loss == float(g[key]), (s_val, loss)
+
+
+def _grid_layer(rng, n, k, group):
+    """W on the 4-bit grid (W = (q - z) s, s of 7 significant bits, codes 0 and 15 in
+    every group), so that quantization reproduces it exactly."""
+    gs = k // group
+    mant = rng.integers(64, 128, size=(gs, n))
+    expo = rng.integers(-10, -6, size=(gs, n))
+    s = np.ldexp(mant.astype(np.float64), expo)
+    z = rng.integers(0, 16, size=(gs, n))
+    q = rng.integers(0, 16, size=(n, k))
+    q[:, 0::group] = 0
+    q[:, 1::group] = 15
+    return (q - np.repeat(z.T, group, axis=1)) * np.repeat(s.T, group, axis=1)
+
+
+def pin_loss_zero_on_grid(o, seed=21, n=8, k=256, group=128):
+    """Closed forms of the objective: it is exactly 0 when W is already on the 4-bit
+    grid and s = 1, and when W diag(s) is on the grid for a power-of-two s that varies
+    from channel to channel (then X diag(s)^-1 and W diag(s) are exact and their
+    products equal those of X and W bit for bit). The same W with s = 1 is off the
+    grid and gives a positive loss."""
+    rng = np.random.default_rng(seed)
+    grid = _grid_layer(rng, n, k, group)
+    x = rng.standard_normal((4, k))
+    assert o.awq_loss(grid, x, np.ones(k), group, o.FMT_ASYM) == 0.0
+    s = np.ldexp(1.0, rng.integers(-2, 3, size=k))         # 1/4 .. 4, per channel
+    w = grid / s[None, :]                                  # exact: powers of two
+    assert np.array_equal(o.fp16_rn(w), w)
+    assert o.awq_loss(w, x, s, group, o.FMT_ASYM) == 0.0
+    assert o.awq_loss(w, x, np.ones(k), group, o.FMT_ASYM) > 0.0
+
+
+def pin_scale_search_finds_exact_exponent(o, seed=22, n=8, k=256, group=128):
+    """A layer that only the exponent alpha = 1 puts on the grid: W = G diag(m)^-1 with
+    G on the grid and channel magnitudes m in {1, 4, 16} that vary within every group,
+    calibration rows of magnitude exactly m (so mean |X_cal| = m). alpha = 1 gives
+    s = m, the fold gives G back exactly and the loss is 0; alpha = 0, 1/4, 1/2, 3/4
+    leave the folded group off the grid, so the search must return alpha = 1."""
+    rng = np.random.default_rng(seed)
+    grid = _grid_layer(rng, n, k, group)
+    m = np.array([1.0, 4.0, 16.0])[rng.integers(0, 3, size=k)]
+    w = grid / m[None, :]
+    assert np.array_equal(o.fp16_rn(w), w)
+    x_cal = m[None, :] * np.where(rng.random((32, k)) < 0.5, -1.0, 1.0)
+    best, losses = o.scale_search(w, x_cal, group, o.FMT_ASYM, grid=4)
+    assert losses.shape == (5,)
+    assert best == 1.0 and losses[4] == 0.0
+    assert np.all(losses[:4] > 0.0)
+
+
 ALL_PINS = [
     pin_fp16_exhaustive, pin_hand_dequant, pin_hand_pack, pin_hand_product,
     pin_hand_requantize, pin_tie_break, pin_on_grid_exact, pin_sym_on_grid,
     pin_degenerate_groups, pin_rtn_error_bound, pin_small_groups, pin_fold_invariance,
     pin_channel_scale, pin_brute_force, pin_pack_roundtrip, pin_layout_orientation,
+    pin_loss_hand_value, pin_loss_zero_on_grid, pin_scale_search_finds_exact_exponent,
 ]
 
 

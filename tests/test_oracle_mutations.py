@@ -177,6 +177,46 @@ def _quantize_no_clamp(w_folded, group=128, fmt=0):
         ao.QMAX = saved
 
 
+def _loss_parts(w, x, s_c, group, fmt, fold=True):
+    x, w, s = ao.as_f64(x), ao.as_f64(w), ao.as_f64(s_c)
+    layer = ao.quantize_layer(w, s if fold else None, group, fmt)
+    return x @ w.T, x, s, layer["w_d"]
+
+
+def _loss_no_sqrt(w, x, s_c, group=128, fmt=0):
+    y, x, s, w_d = _loss_parts(w, x, s_c, group, fmt)
+    return float(np.sum((y - (x / s[None, :]) @ w_d.T) ** 2))
+
+
+def _loss_l1(w, x, s_c, group=128, fmt=0):
+    y, x, s, w_d = _loss_parts(w, x, s_c, group, fmt)
+    return float(np.sum(np.abs(y - (x / s[None, :]) @ w_d.T)))
+
+
+def _loss_x_times_s(w, x, s_c, group=128, fmt=0):
+    y, x, s, w_d = _loss_parts(w, x, s_c, group, fmt)
+    return float(np.sqrt(np.sum((y - (x * s[None, :]) @ w_d.T) ** 2)))
+
+
+def _loss_unfolded_q(w, x, s_c, group=128, fmt=0):
+    # the activations are rescaled but the weights are quantized without the fold
+    y, x, s, w_d = _loss_parts(w, x, s_c, group, fmt, fold=False)
+    return float(np.sqrt(np.sum((y - (x / s[None, :]) @ w_d.T) ** 2)))
+
+
+def _search_argmax(w, x_cal, group=128, fmt=0, grid=20):
+    losses = np.asarray([ao.awq_loss(w, x_cal, ao.channel_scale(x_cal, i / grid)[0], group, fmt)
+                         for i in range(grid + 1)])
+    return int(np.argmax(losses)) / grid, losses
+
+
+def _search_fixed_half(w, x_cal, group=128, fmt=0, grid=20):
+    # every candidate scored with the same alpha = 1/2 scale
+    s, _ = ao.channel_scale(x_cal, 0.5)
+    losses = np.asarray([ao.awq_loss(w, x_cal, s, group, fmt) for _ in range(grid + 1)])
+    return int(np.argmin(losses)) / grid, losses
+
+
 _orig_quantize = ao.quantize_rtn
 
 MUTANTS = {
@@ -202,6 +242,12 @@ MUTANTS = {
     "quantize_scale_unrounded": ("quantize_rtn", _quantize_scale_unrounded),
     "quantize_sym_divides_by_8": ("quantize_rtn", _quantize_sym_over_8),
     "quantize_levels_16": ("quantize_rtn", _quantize_no_clamp),
+    "loss_without_sqrt": ("awq_loss", _loss_no_sqrt),
+    "loss_l1_norm": ("awq_loss", _loss_l1),
+    "loss_multiplies_activations": ("awq_loss", _loss_x_times_s),
+    "loss_quantizes_unfolded_weights": ("awq_loss", _loss_unfolded_q),
+    "search_takes_argmax": ("scale_search", _search_argmax),
+    "search_scores_one_scale": ("scale_search", _search_fixed_half),
 }
 
 
