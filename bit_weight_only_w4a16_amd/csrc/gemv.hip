@@ -77,6 +77,18 @@ __device__ __forceinline__ float row_sum16(float v) {
   return dpp_add<0x140>(v);
 }
 
+// Orders a wavefront's LDS accesses for the compiler: staging stores by some lanes are
+// read back by other lanes of the same wavefront, which a per-lane view of memory does
+// not see as a dependence. A wavefront-scope release/acquire fence pair is an IR-level
+// memory operation (wave_barrier alone is not), so no load is hoisted above it and no
+// store is sunk below it; the hardware executes one wavefront's LDS operations in order,
+// so nothing more is needed.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int M>
 struct XPass {
   uint4 x[M];
@@ -262,13 +274,14 @@ __global__ void __launch_bounds__(WAVES * 64)
       xpass_load(Q, ph0, c, nj);
       xpass_store(Q, c, nj);
     }
-    __builtin_amdgcn_wave_barrier();
+    wave_lds_sync();  // staged X', O, S visible to every lane before the products
     for (int jb = 0; jb < nj; jb += 2 * BATCH) {
       compute(b0, jb, nj);
       load(b0, ph0, jb + 2 * BATCH, nj);
       compute(b1, jb + BATCH, nj);
       load(b1, ph0, jb + 3 * BATCH, nj);
     }
+    wave_lds_sync();  // this phase's reads done before the next phase restages the slots
   }
 
   if constexpr (EXACT) {

@@ -341,7 +341,9 @@ def test_products_deterministic(fn, m):
     d, g, o, y_ref = product_case(n, k, m, 0)
     x = to_dev(d["x"])
     f = awq.awq_gemv if fn == "gemv" else awq.awq_gemm
-    ws = awq.workspace(m, n, k, DEV)     # M = 16: K split across workgroups
+    # 4096 x 4096 at M = 16 runs the decode kernel (no workspace); M = 96 splits K across
+    # narrow-tile workgroups, M = 256 and 512 across wide-tile workgroups
+    ws = awq.workspace(m, n, k, DEV)
     ys = [f(x, g["inv"], g["packed"], n, k, ws=ws) for _ in range(5)]
     torch.cuda.synchronize()
     for y in ys[1:]:
@@ -442,7 +444,7 @@ def test_group_sizes(n, k, group, fmt):
         sc, qz = (g["scales"], g["qzeros"]) if layout == awq.LAYOUT_CANONICAL else (None, None)
         wd = awq.awq_dequant(w, sc, qz, layout, n, k, g_size, fmt)
         assert np.array_equal(bits(wd), f16bits(o["w_d"]))
-    for m in (1, 5, 16):
+    for m in (1, 3, 5, 16):
         x = d["x"][:m]
         y_ref = oracle.matmul_ref(x, o["w_d"], o["inv"])
         ws = awq.workspace(m, n, k, DEV, g_size)
