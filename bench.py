@@ -25,7 +25,9 @@ Also reported (same JSON line):
                     4096 -> 28672, 14336 -> 4096);
   unfused           awq_dequant to binary16 + the library fp16 GEMM (hipBLASLt through
                     torch.matmul) at the same shapes: the unfused baseline;
-  cpu_baseline      the CPU oracle on a bounded sample of the decode workload.
+  ceilings          a read-only kernel streaming each decode shape's weight bytes with the
+                    decode kernel's access pattern, and the cost of an empty launch;
+  cpu_baseline      the CPU oracle on bounded samples of the decode and batched workloads.
 """
 from __future__ import annotations
 
@@ -66,7 +68,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip fused step, batched decode and 70B layers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=8.0)
+    ap.add_argument("--no-ceilings", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=16.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     return ap.parse_args()
@@ -195,18 +198,22 @@ def main():
     t1 = time.perf_counter()
     sec = t1 - t0
     value_gbs = step_bytes * K / sec / 1e9
-    # per-step spread (outside the timed region): each step graph between two events
+    # per-step spread (outside the timed region), in the headline's submission mode: the
+    # graph of `rot` steps replayed between two events, the time divided by `rot`
+    n_spread = max(10, min(50, K // rot))
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
-    for i, (ea, eb) in enumerate(evs):
+           for _ in range(n_spread)]
+    for ea, eb in evs:
         ea.record()
-        g_one[i % rot].replay()
+        g_all.replay()
         eb.record()
     torch.cuda.synchronize()
-    per_step = sorted(ea.elapsed_time(eb) * 1e3 for ea, eb in evs)
-    step_spread = {"median": round(per_step[K // 2], 3),
-                   "p10": round(per_step[K // 10], 3),
-                   "p90": round(per_step[(9 * K) // 10], 3), "steps": K}
+    per_step = sorted(ea.elapsed_time(eb) * 1e3 / rot for ea, eb in evs)
+    step_spread = {"median": round(per_step[n_spread // 2], 3),
+                   "p10": round(per_step[n_spread // 10], 3),
+                   "p90": round(per_step[(9 * n_spread) // 10], 3),
+                   "samples": n_spread, "steps_per_sample": rot,
+                   "submission": "one graph of the rotation's steps, as the headline"}
     del g_all, g_one, evs
 
     # ------------------------------------------- per-kernel durations (HIP events)
@@ -230,6 +237,18 @@ def main():
                                   "launches": 3 * reps * lrot, "weight_copies": lrot}
         del lcp
         torch.cuda.empty_cache()
+    # measured ceilings: a read-only kernel streaming each decode shape's packed weight
+    # bytes with the decode kernel's access pattern, and one empty launch
+    ceil = None
+    if not args.no_ceilings:
+        log("ceilings: streaming read and empty launch")
+        sizes = {name: layers[next(i for i, L in enumerate(layers) if L["name"] == name)]["packed"].numel()
+                 for name in ("q", "gate", "down")}
+        ceil = ceilings(dev, sizes, graph_us, rotation)
+        for name in ("q", "gate", "down"):
+            c = ceil["stream_read"][name]
+            c["decode_over_stream"] = round(c["best_us"] / per_layer[name]["us"], 3)
+
     # The dominant kernel is the decode kernel itself: its 7 launches are the whole step
     # (the 4096 -> 4096 launches alone are 45 % of it). Roofline over one step: the
     # algorithmic bytes of the 7 launches / their summed kernel time, i.e. bytes per
@@ -460,6 +479,7 @@ def main():
                      "kernel": f"awq_gemv M=1, the 7 launches of a step ({sum_kernel_us / 7:.3f} "
                                f"us/launch average, {step_bytes / 7:.0f} B/launch average)"},
         "per_layer_kernel": per_layer,
+        "ceilings": ceil,
         "kernel_sum_us_per_step": round(sum_kernel_us, 3),
         "kernel_only_GB/s": round(step_bytes / sum_kernel_us / 1e3, 1),
         **extra,
@@ -502,44 +522,111 @@ def measured_traffic():
     return int(float(kv["traffic_bytes_per_launch"]))
 
 
+def ceilings(dev, sizes, graph_us, rotation):
+    """Streaming-read ceiling per decode shape (best of the probe's launch shapes, each
+    over its own >1.2 GB of buffers so that no launch reads from the Infinity Cache) and
+    the per-launch cost of an empty kernel, both as back-to-back launches in a graph."""
+    import ctypes
+
+    import torch
+
+    from bit_weight_only_w4a16_amd import build as B
+
+    probe = ctypes.CDLL(B.PROBE_LIB)
+    probe.awq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                            ctypes.c_void_p, ctypes.c_void_p]
+    probe.awq_probe_empty.argtypes = [ctypes.c_void_p]
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+
+    def stream():
+        return torch.cuda.current_stream().cuda_stream
+
+    out = {"stream_read": {}}
+    for name, nbytes in sizes.items():
+        stride = (nbytes + 255) // 256 * 256
+        rot = rotation(stride)
+        buf = torch.empty(rot * stride, dtype=torch.uint8, device=dev)
+        base = buf.data_ptr()
+        per_shape = []
+        for shape in range(probe.awq_probe_shapes()):
+            launches = [lambda r=r, shape=shape: probe.awq_probe_stream_read(
+                base + r * stride, nbytes, shape, sink.data_ptr(), stream()) for r in range(rot)]
+            per_shape.append(round(graph_us(launches, max(2, 1000 // rot)), 3))
+        best = min(per_shape)
+        out["stream_read"][name] = {"bytes": nbytes, "us_per_shape": per_shape, "best_us": best,
+                                    "best_GB/s": round(nbytes / best / 1e3, 1),
+                                    "copies": rot}
+        del buf
+        torch.cuda.empty_cache()
+    out["empty_launch_us"] = round(graph_us([lambda: probe.awq_probe_empty(stream())] * 100, 20), 3)
+    out["what"] = ("read-only kernel over the packed weight bytes of each decode shape, "
+                   "16-byte non-temporal loads, 1 KiB per wavefront load, all loads of a "
+                   "wavefront in flight; empty kernel back to back; graph-timed like the decode "
+                   "kernel")
+    return out
+
+
 def cpu_baseline(seconds: float):
-    """The CPU oracle (as it stands) on the dominant decode layer: dequantize + product,
-    with BLAS on every host core this process may use (at most 16), and on one."""
+    """The CPU oracle (as it stands) on the benchmark's workloads: dequantization and the
+    float64 product timed separately, with BLAS on every CPU thread this process is given
+    (at most 16: the share of host CPUs that comes with one GPU), and on one thread."""
+    import numpy as np
+
     import oracle
     from bit_weight_only_w4a16_amd import synth
     from bit_weight_only_w4a16_amd import roofline as rl
 
-    from threadpoolctl import threadpool_limits
-
-    n, k = 11008, 4096
-    d = synth.layer_inputs(1, 1, n, k, layer=4)
-    s, inv = oracle.channel_scale(d["x_cal"], 0.5)
-    layer = oracle.quantize_layer(d["w"], s, GROUP, oracle.FMT_ASYM)
-    byts = rl.algorithmic_bytes(1, n, k, GROUP, rl.FMT_ASYM, with_inv=True)
-
-    def timed(threads):
-        reps, t = 0, 0.0
-        with threadpool_limits(threads):
-            while t < seconds or reps < 1:
-                t0 = time.perf_counter()
-                w_d = oracle.dequant_packed(layer["qweight"], layer["scales"], layer["qzeros"],
-                                            GROUP, oracle.FMT_ASYM)
-                oracle.matmul_ref(d["x"], w_d, inv)
-                t += time.perf_counter() - t0
-                reps += 1
-        return reps, t
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     cores = max(1, min(16, len(os.sched_getaffinity(0))))
-    reps, t = timed(cores)
-    reps1, t1 = timed(1)
-    return {"value": round(byts * reps / t / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"oracle dequant + float64 product of the 4096->11008 decode layer "
-                      f"(M=1), {reps} repetitions in {t:.1f} s, BLAS limited to {cores} "
-                      f"threads (the dequantization itself is single-threaded numpy)",
-            "ms_per_layer": round(t / reps * 1e3, 1),
-            "single_thread": {"value": round(byts * reps1 / t1 / 1e9, 4), "unit": "GB/s",
-                              "ms_per_layer": round(t1 / reps1 * 1e3, 1)}}
+    blas = [{"api": i.get("internal_api"), "version": i.get("version"),
+             "threads": i.get("num_threads")} for i in threadpool_info()
+            if i.get("user_api") == "blas"]
+
+    def timed(fn, threads, budget):
+        reps, t = 0, 0.0
+        with threadpool_limits(threads):
+            while t < budget or reps < 1:
+                t0 = time.perf_counter()
+                fn()
+                t += time.perf_counter() - t0
+                reps += 1
+        return t / reps
+
+    work = [  # (workload, config index, M, N, K)
+        ("tiny_512x512_m1", 0, 1, 512, 512),
+        ("llama7b_gate_4096x11008_m1", 1, 1, 11008, 4096),
+        ("llama7b_gate_4096x11008_m16", 2, 16, 11008, 4096),
+    ]
+    rows = {}
+    head = None
+    for name, cfg, m, n, k in work:
+        d = synth.layer_inputs(cfg, m, n, k, layer=4 if cfg == 1 else 0)
+        s, inv = oracle.channel_scale(d["x_cal"], 0.5)
+        layer = oracle.quantize_layer(d["w"], s, GROUP, oracle.FMT_ASYM)
+        w_d = oracle.dequant_packed(layer["qweight"], layer["scales"], layer["qzeros"], GROUP,
+                                    oracle.FMT_ASYM)
+        byts = rl.algorithmic_bytes(m, n, k, GROUP, rl.FMT_ASYM, with_inv=True)
+        budget = seconds / (len(work) * 4)
+        deq = lambda: oracle.dequant_packed(layer["qweight"], layer["scales"], layer["qzeros"],
+                                            GROUP, oracle.FMT_ASYM)
+        prod = lambda: oracle.matmul_ref(d["x"], w_d, inv)
+        r = {}
+        for tag, threads in (("all", cores), ("one", 1)):
+            td, tp = timed(deq, threads, budget), timed(prod, threads, budget)
+            r[tag] = {"dequant_ms": round(td * 1e3, 2), "product_ms": round(tp * 1e3, 2),
+                      "GB/s": round(byts / (td + tp) / 1e9, 4),
+                      "GFLOP/s": round(rl.flops(m, n, k) / (td + tp) / 1e9, 3)}
+        rows[name] = r
+        if cfg == 1:
+            head = r["all"]["GB/s"]
+        del d, layer, w_d
+    return {"value": head, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": "the oracle's dequantization and float64 product of one 4096->11008 "
+                      "layer at M=1 (the decode layer the headline step is dominated by); "
+                      f"about {seconds:.0f} s of CPU time over the rows below",
+            "blas": blas, "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "workloads": rows}
 
 
 if __name__ == "__main__":

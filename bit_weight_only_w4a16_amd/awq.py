@@ -269,13 +269,18 @@ _WS = {}
 
 
 def workspace(m: int, n: int, k: int, device, group: int = GROUP) -> torch.Tensor | None:
-    """A workspace large enough for (m, n, k), cached per device and grown on demand
-    (the library overwrites what it uses on every call; no initialisation needed)."""
+    """A workspace large enough for (m, n, k), cached per device and per stream and grown
+    on demand (the library overwrites what it uses on every call, so no initialisation
+    is needed). Calls that share a workspace must be ordered; keying the cache by the
+    current stream keeps layers called on different streams on different buffers. A
+    buffer replaced by a larger one goes back to PyTorch's caching allocator, which hands
+    its memory out again only in the order of that stream."""
     need = awq_workspace_bytes(m, n, k, group)
     if need == 0:
         return None
     dev = torch.device(device)
-    key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
+    index = dev.index if dev.index is not None else torch.cuda.current_device()
+    key = (dev.type, index, torch.cuda.current_stream(index).cuda_stream)
     cur = _WS.get(key)
     if cur is None or cur.numel() < need:
         cur = torch.empty(max(need, 1 << 20), dtype=torch.uint8, device=dev)

@@ -52,9 +52,10 @@ FILE_FLAGS = {
 }
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
+def _compile(src: str, verbose: bool, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src,
+           "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -65,23 +66,47 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(jobs: int = 8, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int = 8, verbose: bool = False, tuning_out: str | None = None) -> str:
+    """Compile and link the library. With `tuning_out`, a separate copy is built at that
+    path with -DAWQ_TUNING, which reads configuration overrides from the environment
+    (for sweeps); the product library next to this file never does."""
+    build_dir = BUILD if tuning_out is None else os.path.join(BUILD, "tuning")
+    extra = () if tuning_out is None else ("-DAWQ_TUNING",)
+    out = LIB if tuning_out is None else os.path.abspath(tuning_out)
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not srcs:
         raise RuntimeError("no HIP sources found")
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, extra), srcs))
+    tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    build_abi_check(verbose)
-    return LIB
+    os.replace(tmp, out)
+    if tuning_out is None:
+        build_probe(verbose)
+        build_abi_check(verbose)
+    return out
+
+
+PROBE_SRC = os.path.join(PKG, "probe", "ceilings.hip")
+PROBE_LIB = os.path.join(PKG, "libawq_probe_gfx950.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The benchmark's ceiling probes (streaming read, empty launch) as their own library."""
+    obj = _compile(PROBE_SRC, verbose)
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", obj, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 ABI_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi", "abi_check.c")
@@ -114,8 +139,10 @@ def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=8)
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--tuning", metavar="PATH",
+                    help="build a copy that reads tuning overrides from the environment, at PATH")
     args = ap.parse_args()
-    print(build(args.jobs, args.verbose))
+    print(build(args.jobs, args.verbose, args.tuning))
 
 
 if __name__ == "__main__":

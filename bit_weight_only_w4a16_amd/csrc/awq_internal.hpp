@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <stdio.h>
+#include <stdlib.h>
+
 #include <atomic>
 
 namespace awq {
@@ -70,6 +73,18 @@ inline hipError_t ensure_lds_limit(const void* kernel, int bytes, std::atomic<ui
   e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
   return e;
+}
+
+// Tuning overrides for configuration sweeps: read from the environment only in a library
+// built with -DAWQ_TUNING (python -m bit_weight_only_w4a16_amd.build --tuning); the
+// product library reads no environment variable and always takes its default choices.
+inline const char* tuning_env(const char* name) {
+#ifdef AWQ_TUNING
+  return getenv(name);
+#else
+  (void)name;
+  return nullptr;
+#endif
 }
 
 // ------------------------------------------------------------ launchers (per file)
@@ -206,6 +221,8 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t m
   return r;
 }
 
+// For pairs that go on through ordinary ALU instructions (dequant_word): the compiler
+// orders those after the asm like any other dependence.
 __device__ __forceinline__ Pairs4 unpack_word(uint32_t w) {
   Pairs4 r;
   const uint32_t w8 = w >> 8;
@@ -213,6 +230,27 @@ __device__ __forceinline__ Pairs4 unpack_word(uint32_t w) {
   r.p[1] = and_or(w, 0x00F000F0u, 0x54005400u);
   r.p[2] = and_or(w8, 0x000F000Fu, 0x64006400u);
   r.p[3] = and_or(w8, 0x00F000F0u, 0x54005400u);
+  return r;
+}
+
+// For pairs that a matrix instruction reads directly. On gfx950 an MFMA may read a VGPR
+// only two wait states after an ALU instruction wrote it; the compiler inserts those
+// waits for the instructions it generates, but it does not treat inline asm as an ALU
+// write, so an MFMA scheduled right behind an asm v_and_or_b32 could read the old
+// register contents (this returned wrong sums in a decode variant where it happened).
+// Here the four v_and_or_b32 are one asm block that ends with s_nop 1: whatever the
+// compiler places next is at least two wait states after the last write. The outputs
+// are early-clobber because the block writes them while still reading its inputs.
+__device__ __forceinline__ Pairs4 unpack_word_mfma(uint32_t w) {
+  Pairs4 r;
+  const uint32_t w8 = w >> 8;
+  asm("v_and_or_b32 %0, %4, %6, %7\n\t"
+      "v_and_or_b32 %1, %4, %8, %9\n\t"
+      "v_and_or_b32 %2, %5, %6, %7\n\t"
+      "v_and_or_b32 %3, %5, %8, %9\n\t"
+      "s_nop 1"
+      : "=&v"(r.p[0]), "=&v"(r.p[1]), "=&v"(r.p[2]), "=&v"(r.p[3])
+      : "v"(w), "v"(w8), "s"(0x000F000Fu), "v"(0x64006400u), "s"(0x00F000F0u), "v"(0x54005400u));
   return r;
 }
 

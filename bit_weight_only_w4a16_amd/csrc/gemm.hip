@@ -419,13 +419,11 @@ hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* p
                        int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt, uint16_t* y,
                        void* ws, size_t ws_bytes, hipStream_t st) {
   // large M: wide wavefront tiles, X' from the workspace (or pre-scaled by the caller).
-  // Tuning overrides for sweeps, read once per process: AWQ_GEMM_WIDE = "0" keeps the
+  // Tuning overrides for sweeps (libraries built for tuning): AWQ_GEMM_WIDE = "0" keeps the
   // narrow kernel, "[splits]<column tiles><K split>" (41, 42, 31, 32, 21, 22, 442, ...)
   // forces a wide configuration.
-  static const int wide_env = [] {
-    const char* w = getenv("AWQ_GEMM_WIDE");
-    return w == nullptr ? -1 : (w[0] == '0' ? 0 : atoi(w));
-  }();
+  const char* wide_str = tuning_env("AWQ_GEMM_WIDE");
+  const int wide_env = wide_str == nullptr ? -1 : (wide_str[0] == '0' ? 0 : atoi(wide_str));
   const bool wide_ok =
       inv_s_c == nullptr || (ws != nullptr && ws_bytes >= static_cast<size_t>(M) * K * 2);
   if (M >= kWideMinM && wide_ok && wide_env != 0) {
@@ -455,29 +453,24 @@ hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* p
   a.splits = 1;
   a.part = nullptr;
   int want = pick_splits(default_blocks(M, N, K), M, N, K, a.n_groups);
-  // AWQ_GEMM_SPLITS = "<splits>" forces the K split (tuning sweeps, read once; needs a
+  // AWQ_GEMM_SPLITS = "<splits>" forces the K split (tuning sweeps; needs a
   // workspace of splits * M * N * 4 bytes, else the product runs unsplit)
-  static const int splits_env = [] {
-    const char* sp = getenv("AWQ_GEMM_SPLITS");
-    return sp == nullptr ? 0 : atoi(sp);
-  }();
+  const char* splits_str = tuning_env("AWQ_GEMM_SPLITS");
+  const int splits_env = splits_str == nullptr ? 0 : atoi(splits_str);
   if (splits_env >= 1 && splits_env <= 16 && splits_env <= a.n_groups) want = splits_env;
   if (want > 1 && ws != nullptr && ws_bytes >= static_cast<size_t>(want) * M * N * sizeof(float)) {
     a.splits = want;
     a.part = static_cast<float*>(ws);
   }
-  // AWQ_GEMM_TILE = "waves_m,wm,wn,sched" selects another tiling (tuning sweeps, read
-  // once)
+  // AWQ_GEMM_TILE = "waves_m,wm,wn,sched" selects another tiling (tuning sweeps)
   struct TileEnv {
     int wv = 0, wm = 0, wn = 0, sc = 0;
     bool set = false;
   };
-  static const TileEnv tile_env = [] {
-    TileEnv t;
-    const char* env = getenv("AWQ_GEMM_TILE");
-    t.set = env != nullptr && sscanf(env, "%d,%d,%d,%d", &t.wv, &t.wm, &t.wn, &t.sc) == 4;
-    return t;
-  }();
+  TileEnv tile_env;
+  if (const char* env = tuning_env("AWQ_GEMM_TILE")) {
+    tile_env.set = sscanf(env, "%d,%d,%d,%d", &tile_env.wv, &tile_env.wm, &tile_env.wn, &tile_env.sc) == 4;
+  }
   if (tile_env.set) {
     const int wv = tile_env.wv, wm = tile_env.wm, wn = tile_env.wn, sc = tile_env.sc;
     if (wv == 1 && wm == 4 && wn == 4 && sc == 0) return launch_tiles<1, 4, 4, 0>(a, st);

@@ -197,7 +197,7 @@ __global__ void __launch_bounds__(WAVES * 64)
         float4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const Pairs4 pr = unpack_word(words[i]);
+          const Pairs4 pr = unpack_word_mfma(words[i]);
           const u32x4_t bw = {pr.p[0], pr.p[1], pr.p[2], pr.p[3]};
           const half8_t af = *reinterpret_cast<const half8_t*>(xg + 8 * i);
           d = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, __builtin_bit_cast(half8_t, bw), d, 0, 0, 0);
@@ -364,16 +364,18 @@ hipError_t launch_m(const MvArgs& a, int64_t n_tiles, hipStream_t st) {
   return launch_cfg<M, 8, 1>(a, n_tiles, st);
 }
 
-// Tuning override for sweeps (M = 1 only), read once per process:
-// AWQ_GEMV_CFG = "waves,batch".
+// Tuning override for sweeps (M = 1 only, libraries built for tuning): AWQ_GEMV_CFG =
+// "waves,batch".
 hipError_t launch_m1(const MvArgs& a, int64_t n_tiles, hipStream_t st) {
-  static const int cfg = [] {
-    const char* env = getenv("AWQ_GEMV_CFG");
+  int cfg = 0;
+  if (const char* env = tuning_env("AWQ_GEMV_CFG")) {
     int w = 0, b = 0;
-    return env != nullptr && sscanf(env, "%d,%d", &w, &b) == 2 ? 10 * w + b : 0;
-  }();
+    if (sscanf(env, "%d,%d", &w, &b) == 2) cfg = 10 * w + b;
+  }
   switch (cfg) {
     case 42: return launch_cfg<1, 4, 2>(a, n_tiles, st);
+    case 44: return launch_cfg<1, 4, 4>(a, n_tiles, st);
+    case 84: return launch_cfg<1, 8, 4>(a, n_tiles, st);
     case 81: return launch_cfg<1, 8, 1>(a, n_tiles, st);
     case 82: return launch_cfg<1, 8, 2>(a, n_tiles, st);
     case 161: return launch_cfg<1, 16, 1>(a, n_tiles, st);

@@ -120,9 +120,13 @@ int awq_pack(const uint16_t* w, const uint16_t* s_c, int64_t N, int64_t K, int32
 size_t awq_repacked_bytes(int64_t N, int64_t K, int32_t group, int32_t fmt);
 
 /*
- * awq_repack - canonical (qweight, scales, qzeros) to the gfx950 packed layout read
- * by awq_gemv, awq_gemm and awq_dequant(AWQ_LAYOUT_GFX950). A pure integer
- * permutation: no value changes. The layout (version awq_layout_version() == 3):
+ * awq_repack - canonical (qweight, scales, qzeros) to the gfx950 packed layout that
+ * awq_gemv, awq_gemm and awq_dequant(AWQ_LAYOUT_GFX950) read (edgesiliconlab ?p=2015,
+ * section "Kernel Execution: Marlin vs. ExLlamaV2 INT4 GEMM Micro-Architecture", item 3:
+ * the 4-bit values are laid out so that a shift and a mask recover them in registers
+ * right before the matrix instruction; the scales and zero points travel with their
+ * block, "The Ultimate Guide to Quantized LLMs: GPTQ", section "Understanding Quantized
+ * Model Compression"). A pure integer permutation: no value changes. The layout (version awq_layout_version() == 3):
  *   rows padded to Np = 16 * ceil(N / 16) (padding rows: codes 0, scale 0, zero 0);
  *   codes  at offset 0: unit (t, g) for t < Np/16, g < K/128 at ((t * K/128) + g) * 1024;
  *          in a unit, lane l (0..63) owns bytes [16 l, 16 l + 16): row n = 16 t + l % 16,
@@ -145,7 +149,10 @@ int awq_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* qz
                size_t packed_bytes, hipStream_t stream);
 
 /*
- * awq_dequant - W_d[n][k] = binary16((q - z) * s), one rounding, bit-exact.
+ * awq_dequant - W_d[n][k] = binary16((q - z) * s), one rounding, bit-exact: the
+ * dequantization of one block with its scaling factor and zero point ("The Ultimate
+ * Guide to Quantized LLMs: GPTQ", section "Understanding Quantized Model Compression").
+ * Used as the parity probe of both layouts and as the unfused baseline's first step.
  * layout AWQ_LAYOUT_CANONICAL: w = qweight, with scales and qzeros (NULL for SYM8).
  * layout AWQ_LAYOUT_GFX950:    w = packed buffer; scales and qzeros must be NULL.
  * w_out  device, [N][K] binary16, written.
@@ -156,7 +163,10 @@ int awq_dequant(const void* w, const uint16_t* scales, const int32_t* qzeros,
                 uint16_t* w_out, hipStream_t stream);
 
 /*
- * Workspace bytes for an M x N x K call of awq_gemv / awq_gemm (0: none used).
+ * Workspace bytes for an M x N x K call of awq_gemv / awq_gemm (0: none used). The pages
+ * define no workspace: it is this library's scratch for splitting K across workgroups
+ * and for the once-per-call X' of the prefill kernel. `group` is the layer's group size
+ * (the same shape checks as the product entry points; 0 for a shape they reject).
  * awq_gemv keeps every partial sum inside a workgroup and uses none. awq_gemm uses it
  *  - at small M, when its output blocks alone would leave CUs idle (and the call does
  *    not run the awq_gemv kernel, see awq_gemm): K is split across workgroups, the

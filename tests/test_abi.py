@@ -36,6 +36,26 @@ def test_every_declared_symbol_is_exported(lib):
     assert sorted(awq.EXPORTS) == names
 
 
+def test_probe_library_exports_its_header():
+    """The benchmark's ceiling probes live in their own library with their own header."""
+    from bit_weight_only_w4a16_amd import build as B
+    if not os.path.exists(B.PROBE_LIB):
+        pytest.skip("probe library not built")
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "awq_probe.h")).read(),
+                  flags=re.S)
+    names = sorted(set(re.findall(r"\b(awq_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["awq_probe_empty", "awq_probe_shapes", "awq_probe_stream_read"]
+    probe = ctypes.CDLL(B.PROBE_LIB)
+    for n in names:
+        assert hasattr(probe, n), n
+    assert probe.awq_probe_shapes() == 4
+    probe.awq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                            ctypes.c_void_p, ctypes.c_void_p]
+    assert probe.awq_probe_stream_read(None, 1024, 0, None, None) == 1   # checked before launch
+    assert probe.awq_probe_stream_read(16, 1 << 31, 0, 16, None) == 1
+    assert probe.awq_probe_stream_read(8, 1024, 0, 16, None) == 3
+
+
 def test_status_strings(lib):
     for code in range(6):
         s = awq.status_string(code)
