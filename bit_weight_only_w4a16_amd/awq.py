@@ -41,6 +41,7 @@ _SIGNATURES = {
     "awq_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "awq_gemv": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _sz, _vp]),
     "awq_gemm": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "awq_gemm_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp]),
     "awq_scale_search_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32]),
     "awq_scale_search": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp, _vp,
                                         _vp, _sz, _vp]),
@@ -233,6 +234,27 @@ def awq_gemm(x, inv_s_c, packed, n: int, k: int, group: int = GROUP, fmt: int = 
              y=None, ws=None) -> torch.Tensor:
     """Matrix-core product, any M >= 1."""
     return _product("awq_gemm", x, inv_s_c, packed, n, k, group, fmt, y, ws)
+
+
+def awq_gemm_noalloc(x, inv_s_c, packed, n: int, k: int, group: int = GROUP,
+                     fmt: int = FMT_ASYM, y=None) -> torch.Tensor:
+    """awq_gemm with the library's own device scratch instead of a caller workspace (the
+    call allocates nothing; pass `y` to allocate nothing on this side either)."""
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    m = x.shape[0]
+    if x.shape[1] != k:
+        raise ValueError("x must have K columns")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float16, device=x.device)
+    _shape(y, "y", (m, n))
+    _shape(inv_s_c, "inv_s_c", (k,))
+    _at_least(packed, "packed", awq_repacked_bytes(n, k, group, fmt))
+    _same_device(x, inv_s_c=inv_s_c, packed=packed, y=y)
+    _check(lib().awq_gemm_noalloc(_dev(x, "x", torch.float16), _opt(inv_s_c, "inv_s_c", torch.float16),
+                                  _dev(packed, "packed", torch.uint8), m, n, k, group, fmt,
+                                  _dev(y, "y", torch.float16), _stream(x.device)), "awq_gemm_noalloc")
+    return y
 
 
 def awq_scale_search_workspace_bytes(rows: int, n: int, k: int, group: int = GROUP,

@@ -26,6 +26,11 @@ int check_shape(int64_t N, int64_t K, int32_t group, int32_t fmt) {
   return AWQ_OK;
 }
 
+}  // namespace
+
+namespace awq {
+
+// Argument checks of the product entry points (also used by awq_gemm_noalloc).
 int check_product(const uint16_t* x, const uint16_t* inv_s_c, const void* packed, int64_t M,
                   int64_t N, int64_t K, int32_t group, int32_t fmt, const uint16_t* y,
                   const void* ws, size_t ws_bytes) {
@@ -42,6 +47,10 @@ int check_product(const uint16_t* x, const uint16_t* inv_s_c, const void* packed
   return AWQ_OK;
 }
 
+}  // namespace awq
+
+namespace {
+using awq::check_product;
 }  // namespace
 
 extern "C" {

@@ -87,6 +87,11 @@ inline const char* tuning_env(const char* name) {
 #endif
 }
 
+// Argument checks shared by the product entry points: an AWQ_* status.
+int check_product(const uint16_t* x, const uint16_t* inv_s_c, const void* packed, int64_t M,
+                  int64_t N, int64_t K, int32_t group, int32_t fmt, const uint16_t* y,
+                  const void* ws, size_t ws_bytes);
+
 // ------------------------------------------------------------ launchers (per file)
 hipError_t launch_channel_scale(const uint16_t* x_cal, int64_t rows, int64_t K, double alpha,
                                 uint16_t* s_c, uint16_t* inv_s_c, hipStream_t st);

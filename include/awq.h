@@ -225,6 +225,25 @@ int awq_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* packed, int
              size_t ws_bytes, hipStream_t stream);
 
 /*
+ * awq_gemm_noalloc - awq_gemm for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments, checks, kernels and results as awq_gemm given a workspace of
+ * awq_workspace_bytes(M, N, K, group) bytes (the same bits), without the workspace
+ * arguments: the library uses a device array of its own, 64 MiB per GPU, which each GPU
+ * the library runs on holds until the process ends (its address is looked up once per
+ * device on the first call there). The call allocates and frees nothing.
+ * Calls whose awq_workspace_bytes exceeds 64 MiB return AWQ_ERR_WORKSPACE before any
+ * launch (use awq_gemm with a caller workspace for those, e.g. M = 4096 on K = 28672).
+ * Every call on one GPU shares that GPU's array and overwrites the part it uses (nothing
+ * in it has to start at zero): calls that overlap on one GPU (different streams, or
+ * host threads without ordering) race and must not be issued.
+ * Errors: INVALID_ARG, UNSUPPORTED, MISALIGNED, WORKSPACE, HIP.
+ */
+int awq_gemm_noalloc(const uint16_t* x, const uint16_t* inv_s_c, const void* packed, int64_t M,
+                     int64_t N, int64_t K, int32_t group, int32_t fmt, uint16_t* y,
+                     hipStream_t stream);
+
+/*
  * Workspace bytes awq_scale_search needs for (rows, N, K, group, fmt); 0 for arguments it
  * would reject.
  */

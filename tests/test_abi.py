@@ -30,7 +30,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(awq.EXPORTS) == names
@@ -54,6 +54,20 @@ def test_probe_library_exports_its_header():
     assert probe.awq_probe_stream_read(None, 1024, 0, None, None) == 1   # checked before launch
     assert probe.awq_probe_stream_read(16, 1 << 31, 0, 16, None) == 1
     assert probe.awq_probe_stream_read(8, 1024, 0, 16, None) == 3
+
+
+def test_gemm_noalloc_checks_before_any_launch(lib):
+    """awq_gemm_noalloc runs awq_gemm's argument checks and refuses a product whose
+    workspace would exceed its 64 MiB device scratch, all before touching the GPU."""
+    f = lib.awq_gemm_noalloc
+    a = 1 << 20   # 16-byte aligned stand-in addresses (never dereferenced)
+    assert f(None, None, a, 4, 4096, 4096, 128, 0, a, None) == INVALID
+    assert f(a, None, a, 4, 4096, 4097, 128, 0, a, None) == INVALID
+    assert f(a + 8, None, a, 4, 4096, 4096, 128, 0, a, None) == MISALIGNED
+    assert f(a, None, a, 4, 4096, 4096, 16, 0, a, None) == UNSUPPORTED
+    assert awq.awq_workspace_bytes(4096, 8192, 28672) > 64 << 20
+    assert f(a, None, a, 4096, 8192, 28672, 128, 0, a, None) == WORKSPACE
+    assert f(a, None, a, 0, 4096, 4096, 128, 0, a, None) == OK   # M = 0: no launch
 
 
 def test_status_strings(lib):
