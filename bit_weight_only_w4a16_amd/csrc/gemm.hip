@@ -25,6 +25,11 @@
 //  * Four wavefronts per workgroup, side by side along N (or 2 x 2); each computes
 //    WM x WN matrix-core tiles of 16 x 16 (up to 128 x 64 outputs, accumulators in
 //    VGPRs), so one dequantized weight fragment feeds WM instructions.
+//  * At small M the weights are the whole cost and the output blocks are few, so K is
+//    split: over KS slices of four wavefronts inside the workgroup (each slice with its
+//    own X' buffers and share of the groups, sums added through LDS in slice order),
+//    and, when even that leaves too few workgroups, across workgroups (float32 partial
+//    sums in the caller's workspace, added in split order by a second launch).
 //  * Workgroups are numbered so that the ones a given XCD (L2 slice) runs are
 //    neighbours along M: they share the same weight columns in that L2.
 #include "awq_internal.hpp"
@@ -58,8 +63,8 @@ struct GemmArgs {
 // them), which the compiler preloads into SGPRs at wavefront launch: no wait for the
 // argument block before the first load. `out` is y (binary16) or, with K split, the
 // float32 partial sums.
-template <int WAVES_M, int WM, int WN, int SCHED, bool ASYM>
-__global__ void __launch_bounds__(kGThreads)
+template <int WAVES_M, int WM, int WN, int SCHED, bool ASYM, int KS>
+__global__ void __launch_bounds__(kGThreads * KS)
     gemm_kernel(const uint16_t* x, const uint16_t* inv, const uint8_t* packed, void* out, int M,
                 int N, int K, int splits, int sets) {
   constexpr int WAVES_N = 4 / WAVES_M;
@@ -85,9 +90,14 @@ __global__ void __launch_bounds__(kGThreads)
   a.sets = sets;
   constexpr int A_VEC = BM * (kGroup / 8) / kGThreads;  // 16-byte X' vectors per thread
   constexpr int BUF = BM * kLdsStride;                  // halfs per LDS buffer
-  extern __shared__ __attribute__((aligned(16))) _Float16 xs[];  // [2][BM][kLdsStride]
+  extern __shared__ __attribute__((aligned(16))) _Float16 xs_all[];  // [KS][2][BM][kLdsStride]
 
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
+  // KS > 1: the workgroup's wavefronts form KS slices of four, each with its own pair of
+  // LDS buffers and its own consecutive share of the workgroup's groups
+  const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
+  const int ks = wave_all >> 2, wave = wave_all & 3;
+  const int tid = threadIdx.x & (kGThreads - 1);  // thread index inside the slice
+  _Float16* xs = xs_all + ks * 2 * BUF;
   const int lane = threadIdx.x & 63;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int r = lane & 15, p = lane >> 4;
@@ -101,9 +111,12 @@ __global__ void __launch_bounds__(kGThreads)
   const int m_blk = bm * BM, n_blk = bn * BN;
   const int ng = a.n_groups;
   const bool has_inv = a.inv != nullptr;
-  // this workgroup's share of K: groups [g0, g1)
+  // this workgroup's share of K: groups [ga, gb); this slice's: [g0, g1), `per` of them
+  // at most (every slice makes the same number of trips, so the barriers match)
   const int split = blockIdx.y;
-  const int g0 = split * ng / a.splits, g1 = (split + 1) * ng / a.splits;
+  const int ga = split * ng / a.splits, gb = (split + 1) * ng / a.splits;
+  const int per = (gb - ga + KS - 1) / KS;
+  const int g0 = min(gb, ga + ks * per), g1 = min(gb, g0 + per);
 
   // one buffer resource over the whole packed layer; this wavefront's weight tiles are
   // addressed by wavefront-uniform (SGPR) offsets (tiles past the last one are clamped:
@@ -131,12 +144,12 @@ __global__ void __launch_bounds__(kGThreads)
   const __amdgpu_buffer_rsrc_t rinv =
       make_rsrc(has_inv ? a.inv : a.x, has_inv ? static_cast<uint32_t>(a.K) * 2 : 0u);
   // thread -> X' vectors: rows tid / 16 + 16 it, channels 8 (tid % 16)..+7 of the group
-  const int a_col = (threadIdx.x & 15) * 8;
+  const int a_col = (tid & 15) * 8;
   uint32_t a_voff[A_VEC];
   int a_lds[A_VEC];
 #pragma unroll
   for (int it = 0; it < A_VEC; ++it) {
-    const int row = (threadIdx.x + it * kGThreads) >> 4;
+    const int row = (tid + it * kGThreads) >> 4;
     a_voff[it] = static_cast<uint32_t>(row * a.K + a_col) * 2;
     a_lds[it] = row * kLdsStride + a_col;
   }
@@ -238,10 +251,11 @@ __global__ void __launch_bounds__(kGThreads)
   // is multiplied, the weights of the next are in flight and its X' goes into the other
   // LDS buffer; one barrier per group.
   // (sched_barrier keeps the scheduler from sinking the prefetches below the math)
-  for (int g = g0; g < g1; g += 2) {
+  for (int t = 0; t < per; t += 2) {
+    const int g = g0 + t;
     load_b(b1, g + 1);
     __builtin_amdgcn_sched_barrier(0);
-    compute(b0, 0);
+    if (g < g1) compute(b0, 0);
     store_a(1);
     load_a(g + 2);
     __builtin_amdgcn_sched_barrier(0);
@@ -253,6 +267,28 @@ __global__ void __launch_bounds__(kGThreads)
     load_a(g + 3);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
+  }
+
+  if constexpr (KS > 1) {
+    // the slices' sums meet in LDS (the X' buffers are free after the last barrier):
+    // slices 1 .. KS-1 write, slice 0 adds them in slice order (the same bits every call)
+    float4_t* red = reinterpret_cast<float4_t*>(xs_all);
+    if (ks > 0) {
+#pragma unroll
+      for (int ms = 0; ms < WM; ++ms)
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+          red[((((ks - 1) * 4 + wave) * WM + ms) * WN + j) * 64 + lane] = acc[ms][j];
+    }
+    __syncthreads();
+    if (ks > 0) return;
+#pragma unroll
+    for (int k2 = 1; k2 < KS; ++k2)
+#pragma unroll
+      for (int ms = 0; ms < WM; ++ms)
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+          acc[ms][j] += red[((((k2 - 1) * 4 + wave) * WM + ms) * WN + j) * 64 + lane];
   }
 
   // epilogue: element q of acc[ms][j] is row 4 (l / 16) + q, column l % 16 of its tile;
@@ -313,25 +349,44 @@ int pick_splits(int64_t blocks, int64_t M, int64_t N, int64_t K, int n_groups) {
   return s < 1 ? 1 : static_cast<int>(s);
 }
 
-template <int WAVES_M, int WM, int WN, int SCHED, bool ASYM>
+template <int WAVES_M, int WM, int WN, int SCHED, bool ASYM, int KS>
 hipError_t launch_tiles_fmt(GemmArgs a, hipStream_t st) {
   constexpr int BM = WAVES_M * WM * 16, BN = (4 / WAVES_M) * WN * 16;
-  const size_t lds = 2ull * BM * kLdsStride * sizeof(_Float16);
+  constexpr size_t lds_x = 2ull * KS * BM * kLdsStride * sizeof(_Float16);
+  constexpr size_t lds_red = (KS - 1) * 4ull * WM * WN * 64 * 16;
+  const size_t lds = lds_x > lds_red ? lds_x : lds_red;
   static std::atomic<uint64_t> lds_done{0};
   const hipError_t ea = ensure_lds_limit(
-      reinterpret_cast<const void*>(&gemm_kernel<WAVES_M, WM, WN, SCHED, ASYM>), static_cast<int>(lds),
+      reinterpret_cast<const void*>(&gemm_kernel<WAVES_M, WM, WN, SCHED, ASYM, KS>), static_cast<int>(lds),
       lds_done);
   if (ea != hipSuccess) return ea;
   a.n_blocks_m = (a.M + BM - 1) / BM;
   a.n_blocks_n = (a.N + BN - 1) / BN;
   const unsigned blocks = static_cast<unsigned>(a.n_blocks_m) * static_cast<unsigned>(a.n_blocks_n);
   void* out = a.splits > 1 ? static_cast<void*>(a.part) : static_cast<void*>(a.y);
-  hipLaunchKernelGGL((gemm_kernel<WAVES_M, WM, WN, SCHED, ASYM>), dim3(blocks, a.splits),
-                     dim3(kGThreads), lds, st, a.x, a.inv, a.packed, out, a.M, a.N, a.K, a.splits,
+  hipLaunchKernelGGL((gemm_kernel<WAVES_M, WM, WN, SCHED, ASYM, KS>), dim3(blocks, a.splits),
+                     dim3(kGThreads * KS), lds, st, a.x, a.inv, a.packed, out, a.M, a.N, a.K, a.splits,
                      a.sets);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   return launch_splitk_reduce(a.part, a.splits, static_cast<int64_t>(a.M) * a.N, a.y, st);
+}
+
+// How the narrow tiles split K (from sweeps on MI355X at M = 8 .. 64 on the 7B and 70B
+// layers): S = pick_splits splits in all; with at least 80 output blocks they are taken
+// inside the workgroup (two or four slices of four wavefronts, partial sums added
+// through LDS, one launch: 8-15 % faster on 4096 -> 11008 and 8192 -> 28672), with fewer
+// blocks two slices and up to four workgroups per block (the partial sums of the
+// workgroups go through the workspace and a second launch; 0-10 % faster than eight
+// workgroups). Four slices only for wavefront tiles of at most four matrix-core tiles.
+struct NarrowSplit {
+  int ks, splits;
+};
+NarrowSplit pick_narrow(int64_t blocks, int64_t M, int64_t N, int64_t K, int n_groups, int tiles) {
+  const int s = pick_splits(blocks, M, N, K, n_groups);
+  if (s <= 1) return {1, 1};
+  if (blocks >= 80) return {s >= 3 && tiles <= 4 ? 4 : 2, 1};
+  return {2, s < 4 ? s : 4};
 }
 
 // Output blocks of the default tiling for an M x N product (see launch_gemm).
@@ -340,6 +395,13 @@ int64_t blocks_of(int64_t M, int64_t N) {
   constexpr int BM = WAVES_M * WM * 16, BN = (4 / WAVES_M) * WN * 16;
   return ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
 }
+// matrix-core tiles per wavefront of the default small-M tiling (M <= 64)
+int default_wave_tiles(int64_t M, int64_t N, int64_t K) {
+  if (M <= 16) return N * K <= (int64_t{1} << 26) ? 1 : 2;
+  if (M <= 32) return N * K <= (int64_t{1} << 26) ? 2 : 4;
+  return N * K <= (int64_t{1} << 26) ? 4 : 8;
+}
+
 int64_t default_blocks(int64_t M, int64_t N, int64_t K) {
   if (M <= 16 && N * K <= (int64_t{1} << 26)) return blocks_of<1, 1, 1>(M, N);
   if (M <= 16) return blocks_of<1, 1, 2>(M, N);
@@ -351,10 +413,22 @@ int64_t default_blocks(int64_t M, int64_t N, int64_t K) {
   return blocks_of<1, 4, 4>(M, N);
 }
 
-template <int WAVES_M, int WM, int WN, int SCHED = 0>
+template <int WAVES_M, int WM, int WN, int SCHED = 0, int KS = 1>
 hipError_t launch_tiles(GemmArgs a, hipStream_t st) {
-  if (a.zeros_off >= 0) return launch_tiles_fmt<WAVES_M, WM, WN, SCHED, true>(a, st);
-  return launch_tiles_fmt<WAVES_M, WM, WN, SCHED, false>(a, st);
+  if (a.zeros_off >= 0) return launch_tiles_fmt<WAVES_M, WM, WN, SCHED, true, KS>(a, st);
+  return launch_tiles_fmt<WAVES_M, WM, WN, SCHED, false, KS>(a, st);
+}
+
+// the small-M tilings with K also split inside the workgroup (KS slices of four wavefronts)
+template <int WAVES_M, int WM, int WN>
+hipError_t launch_tiles_ks(GemmArgs a, int ks, hipStream_t st) {
+  // four slices (1024 threads, 128 VGPRs per lane) only for wavefront tiles of at most
+  // four matrix-core tiles: larger ones would spill
+  if constexpr (WM * WN <= 4) {
+    if (ks == 4) return launch_tiles<WAVES_M, WM, WN, 0, 4>(a, st);
+  }
+  if (ks >= 2) return launch_tiles<WAVES_M, WM, WN, 0, 2>(a, st);
+  return launch_tiles<WAVES_M, WM, WN, 0, 1>(a, st);
 }
 
 template <int S>
@@ -411,7 +485,10 @@ constexpr int64_t kWideMinM = 256;
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M >= kWideMinM) return gemm_wide_workspace_bytes(M, N, K);
   if (small_m_takes_decode_kernel(M, N, K)) return 0;
-  const int s = pick_splits(default_blocks(M, N, K), M, N, K, static_cast<int>(K / kGroup));
+  const int64_t blocks = default_blocks(M, N, K);
+  const int n_groups = static_cast<int>(K / kGroup);
+  const int s = M <= 64 ? pick_narrow(blocks, M, N, K, n_groups, default_wave_tiles(M, N, K)).splits
+                        : pick_splits(blocks, M, N, K, n_groups);
   return s > 1 ? static_cast<size_t>(s) * M * N * sizeof(float) : 0;
 }
 
@@ -452,12 +529,28 @@ hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* p
   // for the partial sums (without one the product runs unsplit)
   a.splits = 1;
   a.part = nullptr;
-  int want = pick_splits(default_blocks(M, N, K), M, N, K, a.n_groups);
+  const int64_t blocks = default_blocks(M, N, K);
+  int want = pick_splits(blocks, M, N, K, a.n_groups);
+  int ks = 1;
+  if (M <= 64) {
+    const NarrowSplit ns = pick_narrow(blocks, M, N, K, a.n_groups, default_wave_tiles(M, N, K));
+    ks = ns.ks;
+    want = ns.splits;
+  }
   // AWQ_GEMM_SPLITS = "<splits>" forces the K split (tuning sweeps; needs a
   // workspace of splits * M * N * 4 bytes, else the product runs unsplit)
   const char* splits_str = tuning_env("AWQ_GEMM_SPLITS");
   const int splits_env = splits_str == nullptr ? 0 : atoi(splits_str);
   if (splits_env >= 1 && splits_env <= 16 && splits_env <= a.n_groups) want = splits_env;
+  // AWQ_GEMM_KS = "<slices>,<splits>" (tuning sweeps): K split inside the workgroup over
+  // 1, 2 or 4 slices of four wavefronts, and across <splits> workgroups
+  if (const char* e = tuning_env("AWQ_GEMM_KS")) {
+    int k1 = 1, s1 = 1;
+    if (sscanf(e, "%d,%d", &k1, &s1) == 2 && (k1 == 1 || k1 == 2 || k1 == 4) && s1 >= 1 && s1 <= 16) {
+      ks = k1;
+      want = s1;
+    }
+  }
   if (want > 1 && ws != nullptr && ws_bytes >= static_cast<size_t>(want) * M * N * sizeof(float)) {
     a.splits = want;
     a.part = static_cast<float*>(ws);
@@ -500,12 +593,12 @@ hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* p
   // the workgroups cover the CUs about 2.5 times; at larger M a 64 x 256 tile (each wavefront
   // 64 x 64) runs best, or for long K or wide N a 128 x 128 tile (each wavefront 128 x
   // 32), which dequantizes each weight fragment for 8 row tiles.
-  if (M <= 16 && N * K <= (int64_t{1} << 26)) return launch_tiles<1, 1, 1>(a, st);
-  if (M <= 16) return launch_tiles<1, 1, 2>(a, st);
-  if (M <= 32 && N * K <= (int64_t{1} << 26)) return launch_tiles<1, 2, 1>(a, st);
-  if (M <= 32) return launch_tiles<1, 2, 2>(a, st);
-  if (M <= 64 && N * K <= (int64_t{1} << 26)) return launch_tiles<1, 2, 2>(a, st);
-  if (M <= 64) return launch_tiles<1, 4, 2>(a, st);
+  if (M <= 16 && N * K <= (int64_t{1} << 26)) return launch_tiles_ks<1, 1, 1>(a, ks, st);
+  if (M <= 16) return launch_tiles_ks<1, 1, 2>(a, ks, st);
+  if (M <= 32 && N * K <= (int64_t{1} << 26)) return launch_tiles_ks<1, 2, 1>(a, ks, st);
+  if (M <= 32) return launch_tiles_ks<1, 2, 2>(a, ks, st);
+  if (M <= 64 && N * K <= (int64_t{1} << 26)) return launch_tiles_ks<1, 2, 2>(a, ks, st);
+  if (M <= 64) return launch_tiles_ks<1, 4, 2>(a, ks, st);
   if (K >= 8192 || N >= 16384) return launch_tiles<1, 8, 2>(a, st);
   return launch_tiles<1, 4, 4>(a, st);
 }

@@ -168,10 +168,13 @@ int awq_dequant(const void* w, const uint16_t* scales, const int32_t* qzeros,
  * and for the once-per-call X' of the prefill kernel. `group` is the layer's group size
  * (the same shape checks as the product entry points; 0 for a shape they reject).
  * awq_gemv keeps every partial sum inside a workgroup and uses none. awq_gemm uses it
- *  - at small M, when its output blocks alone would leave CUs idle (and the call does
- *    not run the awq_gemv kernel, see awq_gemm): K is split across workgroups, the
- *    float32 partial sums [splits][M][N] go to the workspace and a second kernel adds
- *    them in split order;
+ *  - at small M (up to 64 rows, when the call does not run the awq_gemv kernel, see
+ *    awq_gemm), when the output has fewer than 80 blocks of its tiling: K is split
+ *    across up to four workgroups per block (and in two inside each), the float32 partial
+ *    sums [splits][M][N] go to the workspace and a second kernel adds them in split
+ *    order (with more blocks K is split only inside the workgroup: no workspace);
+ *  - at 65 <= M < 256 when the output blocks alone would leave CUs idle: the same, with
+ *    up to eight workgroups per block;
  *  - at M >= 256 with inv_s_c given: X' = binary16(X * inv_s_c) is formed once into the
  *    workspace ([M][K] binary16) and the wide-tile kernel streams it into LDS;
  *  - at M >= 256 when the 128 x 256 output blocks cover fewer than half of the CUs: K is

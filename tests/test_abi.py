@@ -93,9 +93,11 @@ def test_sizes():
     assert awq.awq_repacked_bytes(64, 256, 32) == 8192 + 1024 + 256
     assert awq.awq_repacked_bytes(64, 256, 256) == awq.awq_repacked_bytes(64, 256, 128)
     assert awq.awq_workspace_bytes(0, 4096, 4096) == 0
-    # split-K partial sums only where the output blocks alone leave CUs idle
-    assert awq.awq_workspace_bytes(16, 11008, 4096) % (16 * 11008 * 4) == 0
-    assert awq.awq_workspace_bytes(16, 11008, 4096) > 0
+    # partial sums in the workspace only where few output blocks need K split across
+    # workgroups (4096 output columns at M = 16: 64 blocks, four workgroups per block);
+    # with many blocks (11008 columns) K is split inside the workgroup, no workspace
+    assert awq.awq_workspace_bytes(16, 4096, 11008) == 4 * 16 * 4096 * 4
+    assert awq.awq_workspace_bytes(16, 11008, 4096) == 0
     # up to 16 rows on at most 256 row tiles the decode kernel runs: no workspace
     assert awq.awq_workspace_bytes(16, 4096, 4096) == 0
     assert awq.awq_workspace_bytes(8, 4096, 11008) == 0
