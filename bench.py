@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--no-gemm", action="store_true", help="skip prefill GEMM and unfused")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip fused step, batched decode and 70B layers")
+    ap.add_argument("--only-extra", default="",
+                    help="comma-separated extra sections to run (fused_step, batched, llama70b, "
+                         "group_sizes, scale_search); default all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=16.0)
@@ -260,7 +263,12 @@ def main():
     torch.cuda.empty_cache()
 
     extra = {}
-    if not args.no_extra:
+    only = {t for t in args.only_extra.split(",") if t}
+
+    def want(section):
+        return not args.no_extra and (not only or section in only)
+
+    if want("fused_step"):
         # -------------------------------------- fused q|k|v and gate|up: four launches
         log("fused decode step (4 launches)")
         fl = [make_layer(1, n, k, layer=20 + j) for j, (_, n, k) in enumerate(FUSED_LAYERS)]
@@ -284,6 +292,7 @@ def main():
         del f_cp, fl, launches
         torch.cuda.empty_cache()
 
+    if want("batched"):
         # -------------------------------------- batched decode M = 8 .. 64, 4096 -> 11008
         log("batched decode")
         bl = make_layer(2, 11008, 4096, m=max(BATCHED_M))
@@ -305,6 +314,7 @@ def main():
         del b_cp, bl, xall
         torch.cuda.empty_cache()
 
+    if want("llama70b"):
         # -------------------------------------- 70B layers, M = 1, 16, 256, 4096
         log("70B layers")
         rows70, rows70b = [], []
@@ -339,6 +349,7 @@ def main():
         extra["llama70b_m1"] = rows70
         extra["llama70b_batched"] = rows70b
 
+    if want("group_sizes"):
         # -------------------------------------- group sizes (NEXT-4): 4096 -> 11008, M = 1
         log("group sizes")
         gs_rows = []
@@ -364,6 +375,7 @@ def main():
             torch.cuda.empty_cache()
         extra["group_sizes"] = {"shape": "4096->11008", "M": 1, "rows": gs_rows}
 
+    if want("scale_search"):
         # -------------------------------------- AWQ exponent search (NEXT-1), one 7B layer
         log("AWQ scale search")
         d = synth.layer_inputs(1, 1, 11008, 4096, layer=4)

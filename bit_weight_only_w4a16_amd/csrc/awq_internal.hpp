@@ -129,6 +129,19 @@ hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* p
                        void* ws, size_t ws_bytes, hipStream_t st);
 
 // ------------------------------------------------------------------ device helpers
+// Workgroups are dealt to the 8 XCDs (each with its own L2) round-robin by workgroup
+// number: workgroup i runs on XCD i % 8. Output block numbers are handed out so that
+// each XCD gets a contiguous run of them (XCD x the blocks [x q + min(x, r), ...) with
+// q = nb / 8, r = nb % 8, one more for the first r XCDs): a kernel that walks blocks down
+// M first then keeps the blocks that share weight columns in one L2. A bijection on
+// [0, nb) for any nb.
+__device__ __forceinline__ int xcd_block(int i, int nb) {
+  constexpr int kXcd = 8;
+  const int q = nb / kXcd, r = nb % kXcd;
+  const int x = i % kXcd, slot = i / kXcd;
+  return x * q + (x < r ? x : r) + slot;
+}
+
 // Buffer resource over [base, base + bytes): loads take a wavefront-uniform SGPR offset
 // plus a per-lane VGPR offset, so streaming through the weights costs no 64-bit address
 // arithmetic; an offset past `bytes` reads 0. Word 3 is the gfx9 raw-buffer format.

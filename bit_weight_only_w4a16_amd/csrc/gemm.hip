@@ -42,7 +42,6 @@ namespace {
 
 constexpr int kLdsStride = kGroup + 8;  // halfs per LDS row (16-byte pad)
 constexpr int kGThreads = 256;
-constexpr int kXcds = 8;
 
 struct GemmArgs {
   const uint16_t* x;
@@ -105,8 +104,7 @@ __global__ void __launch_bounds__(kGThreads * KS)
   // workgroup -> output block. Blocks are dealt to the XCDs round-robin; renumber so
   // that each XCD gets a contiguous run, walked down M first (shared weight columns).
   const int nb = a.n_blocks_m * a.n_blocks_n;
-  int bid = blockIdx.x;
-  if (nb % kXcds == 0) bid = (bid % kXcds) * (nb / kXcds) + bid / kXcds;
+  const int bid = xcd_block(blockIdx.x, nb);
   const int bm = bid % a.n_blocks_m, bn = bid / a.n_blocks_m;
   const int m_blk = bm * BM, n_blk = bn * BN;
   const int ng = a.n_groups;

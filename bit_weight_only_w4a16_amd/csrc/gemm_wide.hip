@@ -34,7 +34,6 @@ namespace {
 constexpr int kBM = 128;              // rows of X' per workgroup
 constexpr int kRowBytes = kGroup * 2;  // one activation row of a group: 256 B
 constexpr int kTileBytes = kBM * kRowBytes;
-constexpr int kXcds = 8;
 
 struct WideArgs {
   const uint16_t* xs;  // X' [M][K] binary16
@@ -75,8 +74,7 @@ __global__ void __launch_bounds__(256 * KS) gemm_wide_kernel(WideArgs a) {
   const int r = lane & 15, p = lane >> 4;
 
   const int nb = a.n_blocks_m * a.n_blocks_n;
-  int bid = blockIdx.x;
-  if (nb % kXcds == 0) bid = (bid % kXcds) * (nb / kXcds) + bid / kXcds;
+  const int bid = xcd_block(blockIdx.x, nb);
   const int bm = bid % a.n_blocks_m, bn = bid / a.n_blocks_m;
   const int m_blk = bm * kBM, n_blk = bn * BN;
   const int ng = a.n_groups;
