@@ -46,6 +46,8 @@ DECODE_LAYERS = [  # (name, N, K)
     ("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),
     ("gate", 11008, 4096), ("up", 11008, 4096), ("down", 4096, 11008),
 ]
+# the block's dependencies, in DECODE_LAYERS order (q, k, v, o, gate, up, down)
+CHAIN_SRCS = [-1, -1, -1, 2, 3, 3, 5]
 FUSED_LAYERS = [("qkv", 12288, 4096), ("o", 4096, 4096), ("gate_up", 22016, 4096),
                 ("down", 4096, 11008)]
 PREFILL_LAYERS = [("qkv", 6144, 4096), ("gate_up", 28672, 4096), ("down", 4096, 14336)]
@@ -290,6 +292,60 @@ def main():
                                     "bound_at_8TB/s": round(rl.max_tokens_per_s(
                                         rl.HBM_PEAK_GBS, N_BLOCKS_7B * step_bytes / 1e9), 1)}}
         del f_cp, fl, launches
+        torch.cuda.empty_cache()
+
+    if want("chain_step"):
+        # ------------------------- the decoder block as one awq_gemv_chain launch (NEXT-2)
+        # the seven products with the block's dependencies (q, k, v read x; o reads v;
+        # gate and up read o; down reads up), one launch per step over rotating weights;
+        # beside it the same launch with every layer reading x (no waits inside), and both
+        # submitted eagerly (no graph) against seven eager awq_gemv launches
+        log("decoder block as one launch (awq_gemv_chain)")
+        cl = [make_layer(1, n, k, layer=30 + j) for j, (_, n, k) in enumerate(DECODE_LAYERS)]
+        c_bytes = sum(rl.algorithmic_bytes(1, L["n"], L["k"], GROUP, rl.FMT_ASYM, True) for L in cl)
+        c_rot = rotation(sum(L["packed"].numel() for L in cl))
+        c_cp = [[L["packed"]] + [L["packed"].clone() for _ in range(c_rot - 1)] for L in cl]
+        state = awq.chain_state(dev)
+
+        def chain_specs(r, srcs):
+            return [{"packed": c_cp[j][r], "n": L["n"], "k": L["k"], "inv_s_c": L["inv"],
+                     "y": L["y"], "src": srcs[j], **({"x": L["x"]} if srcs[j] < 0 else {})}
+                    for j, L in enumerate(cl)]
+
+        res = {}
+        for tag, srcs in (("block", CHAIN_SRCS), ("independent", [-1] * len(cl))):
+            specs = [chain_specs(r, srcs) for r in range(c_rot)]
+            us = graph_us([(lambda sp=sp: awq.awq_gemv_chain(sp, state)) for sp in specs],
+                          max(2, K // c_rot))
+            res[tag] = {"us_per_step": round(us, 3), "GB/s": round(c_bytes / us / 1e3, 1)}
+            # eager submission through the Python binding, no graph: host cost included
+            torch.cuda.synchronize()
+            n_eager = max(20, K)
+            t0 = time.perf_counter()
+            for i in range(n_eager):
+                awq.awq_gemv_chain(specs[i % c_rot], state)
+            torch.cuda.synchronize()
+            res[tag]["eager_us_per_step"] = round((time.perf_counter() - t0) / n_eager * 1e6, 3)
+        ws = None
+        for L in cl:
+            ws = awq.workspace(1, L["n"], L["k"], dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(max(20, K)):
+            for j, L in enumerate(cl):
+                awq.awq_gemv(L["x"], L["inv"], c_cp[j][i % c_rot], L["n"], L["k"], GROUP,
+                             awq.FMT_ASYM, y=L["y"], ws=ws)
+        torch.cuda.synchronize()
+        sep_eager = (time.perf_counter() - t0) / max(20, K) * 1e6
+        torch.cuda.synchronize()
+        errors = awq.chain_errors(state)
+        extra["chain_step"] = {
+            "entry": "awq_gemv_chain", "launches_per_step": 1,
+            "dependencies": "q, k, v <- x; o <- v; gate, up <- o; down <- up",
+            **res, "seven_launches_eager_us_per_step": round(sep_eager, 3),
+            "waits_timed_out": errors,
+            "linear_tok_per_s_7b": round(1e6 / (N_BLOCKS_7B * res["block"]["us_per_step"]), 1)}
+        del c_cp, cl, state
         torch.cuda.empty_cache()
 
     if want("batched"):

@@ -45,8 +45,19 @@ _SIGNATURES = {
     "awq_scale_search_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32]),
     "awq_scale_search": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp, _vp,
                                         _vp, _sz, _vp]),
+    "awq_chain_state_bytes": (_sz, []),
+    "awq_gemv_chain": (ctypes.c_int, [_vp, _i32, _vp, _vp]),
 }
 EXPORTS = tuple(_SIGNATURES)
+
+
+class ChainLayer(ctypes.Structure):
+    """awq_chain_layer of awq.h."""
+    _fields_ = [("x", _vp), ("inv_s_c", _vp), ("packed", _vp), ("y", _vp), ("N", _i64),
+                ("K", _i64), ("group", _i32), ("fmt", _i32), ("src", _i32), ("reserved", _i32)]
+
+
+CHAIN_MAX_LAYERS = 8
 
 
 class AwqError(RuntimeError):
@@ -283,6 +294,65 @@ def awq_scale_search(w, x_cal, group: int = GROUP, fmt: int = FMT_ASYM, grid: in
                                   best.data_ptr(), _dev(ws, "ws", torch.uint8), ws.numel(),
                                   _stream(w.device)), "awq_scale_search")
     return best, losses
+
+
+def awq_chain_state_bytes() -> int:
+    return int(lib().awq_chain_state_bytes())
+
+
+def chain_state(device) -> torch.Tensor:
+    """A zeroed state buffer for awq_gemv_chain (one per stream that runs chains)."""
+    return torch.zeros(awq_chain_state_bytes(), dtype=torch.uint8, device=device)
+
+
+def chain_errors(state: torch.Tensor) -> int:
+    """Waits that ran out in the chain calls since the state was last cleared (word 0;
+    synchronises with the device)."""
+    return int(state[:4].view(torch.int32).item())
+
+
+def awq_gemv_chain(layers, state: torch.Tensor):
+    """Run M = 1 products in one launch. `layers` is a list of dicts with keys packed, n,
+    k and optionally x ([K] or [1, K] fp16; required when src is -1), inv_s_c, group,
+    fmt, y ([N] or [1, N] fp16, allocated when absent) and src (index of an earlier
+    layer whose output is this layer's input, default -1). Returns the outputs, [1, N]
+    each."""
+    n_layers = len(layers)
+    if n_layers > CHAIN_MAX_LAYERS:
+        raise ValueError(f"at most {CHAIN_MAX_LAYERS} layers per call")
+    _dev(state, "state", torch.uint8)
+    _at_least(state, "state", awq_chain_state_bytes())
+    arr = (ChainLayer * max(n_layers, 1))()
+    outs = []
+    for i, spec in enumerate(layers):
+        n, k = int(spec["n"]), int(spec["k"])
+        group, fmt = int(spec.get("group", GROUP)), int(spec.get("fmt", FMT_ASYM))
+        src = int(spec.get("src", -1))
+        x, inv, packed, y = spec.get("x"), spec.get("inv_s_c"), spec["packed"], spec.get("y")
+        if not -1 <= src < i:
+            raise ValueError(f"layer {i}: src must be -1 or an earlier layer")
+        if src >= 0:
+            if int(layers[src]["n"]) != k:
+                raise ValueError(f"layer {i}: its input (layer {src}) has N != K")
+            x = None
+        elif x is None:
+            raise ValueError(f"layer {i}: x is required when src is -1")
+        else:
+            x = x.reshape(-1)
+            _shape(x, f"layers[{i}].x", (k,))
+        if y is None:
+            y = torch.empty((1, n), dtype=torch.float16, device=state.device)
+        _shape(y.reshape(-1), f"layers[{i}].y", (n,))
+        _shape(inv, f"layers[{i}].inv_s_c", (k,))
+        _at_least(packed, f"layers[{i}].packed", awq_repacked_bytes(n, k, group, fmt))
+        _same_device(state, x=x, inv_s_c=inv, packed=packed, y=y)
+        arr[i] = ChainLayer(_opt(x, "x", torch.float16), _opt(inv, "inv_s_c", torch.float16),
+                            _dev(packed, "packed", torch.uint8), _dev(y, "y", torch.float16),
+                            n, k, group, fmt, src, 0)
+        outs.append(y.reshape(1, n))
+    _check(lib().awq_gemv_chain(ctypes.cast(arr, _vp), n_layers, state.data_ptr(),
+                                _stream(state.device)), "awq_gemv_chain")
+    return outs
 
 
 # --------------------------------------------------------------------- convenience

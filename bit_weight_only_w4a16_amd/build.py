@@ -49,6 +49,7 @@ FILE_FLAGS = {
     "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=16"],
     "gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=16"],
     "gemm_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=16"],
+    "chain.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

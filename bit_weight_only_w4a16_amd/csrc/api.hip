@@ -161,6 +161,33 @@ int awq_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* packed, int
   return hip_status(awq::launch_gemm(x, inv_s_c, packed, M, N, K, group, fmt, y, ws, ws_bytes, stream));
 }
 
+size_t awq_chain_state_bytes(void) { return awq::chain_state_bytes(); }
+
+int awq_gemv_chain(const awq_chain_layer* layers, int32_t n_layers, void* state,
+                   hipStream_t stream) {
+  if (n_layers < 0) return AWQ_ERR_INVALID_ARG;
+  if (n_layers == 0) return AWQ_OK;
+  if (layers == nullptr || state == nullptr) return AWQ_ERR_INVALID_ARG;
+  if (n_layers > awq::chain_max_layers()) return AWQ_ERR_UNSUPPORTED;
+  for (int i = 0; i < n_layers; ++i) {
+    const awq_chain_layer& l = layers[i];
+    int rc = check_shape(l.N, l.K, l.group, l.fmt);
+    if (rc != AWQ_OK) return rc;
+    if (l.packed == nullptr || l.y == nullptr) return AWQ_ERR_INVALID_ARG;
+    if (l.src < -1 || l.src >= i) return AWQ_ERR_INVALID_ARG;
+    if (l.src == -1 && l.x == nullptr) return AWQ_ERR_INVALID_ARG;
+    if (l.src >= 0 && layers[l.src].N != l.K) return AWQ_ERR_INVALID_ARG;
+    // every wavefront of a workgroup takes at least one 128-channel unit of a tile, and
+    // the staged inputs fit in LDS
+    if (l.group < kGroup || l.K < awq::chain_min_k() || l.K > awq::chain_max_k()) return AWQ_ERR_UNSUPPORTED;
+    if ((l.src == -1 && !aligned16(l.x)) || !aligned16(l.inv_s_c) || !aligned16(l.packed) ||
+        !aligned16(l.y))
+      return AWQ_ERR_MISALIGNED;
+  }
+  if (!aligned16(state)) return AWQ_ERR_MISALIGNED;
+  return hip_status(awq::launch_chain(layers, n_layers, static_cast<uint32_t*>(state), stream));
+}
+
 size_t awq_scale_search_workspace_bytes(int64_t rows, int64_t N, int64_t K, int32_t group,
                                         int32_t fmt) {
   if (rows < 1 || rows > 256 || check_shape(N, K, group, fmt) != AWQ_OK) return 0;

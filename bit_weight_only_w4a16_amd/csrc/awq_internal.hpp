@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/awq.h"
+
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -127,6 +129,12 @@ hipError_t launch_gemm_wide(const uint16_t* x, const uint16_t* inv_s_c, const vo
 hipError_t launch_gemm(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
                        int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt, uint16_t* y,
                        void* ws, size_t ws_bytes, hipStream_t st);
+
+size_t chain_state_bytes();
+int chain_max_layers();
+int chain_max_k();
+int chain_min_k();
+hipError_t launch_chain(const awq_chain_layer* layers, int n, uint32_t* state, hipStream_t st);
 
 // ------------------------------------------------------------------ device helpers
 // Workgroups are dealt to the 8 XCDs (each with its own L2) round-robin by workgroup

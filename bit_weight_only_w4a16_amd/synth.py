@@ -59,3 +59,22 @@ def layer_inputs(config: int, m: int, n: int, k: int, layer: int = 0) -> dict:
         "x_cal": activations(CAL_ROWS, k, SEED_XCAL + off, outl),
         "outliers": outl,
     }
+
+
+def signed_permutation(n: int, seed: int, value: float) -> np.ndarray:
+    """fp16 [n, n] with one nonzero per row, +-value at a random permuted column."""
+    rng = np.random.default_rng(seed)
+    cols = rng.permutation(n)
+    signs = rng.choice(np.array([-1.0, 1.0]), n)
+    w = np.zeros((n, n), dtype=np.float32)
+    w[np.arange(n), cols] = signs * value
+    return w.astype(np.float16)
+
+
+def sparse_signs(k: int, count: int, seed: int) -> np.ndarray:
+    """fp16 [1, k]: `count` entries of +-1 at random positions, zeros elsewhere."""
+    rng = np.random.default_rng(seed)
+    x = np.zeros((1, k), dtype=np.float32)
+    pos = rng.choice(k, count, replace=False)
+    x[0, pos] = rng.choice(np.array([-1.0, 1.0]), count)
+    return x.astype(np.float16)

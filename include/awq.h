@@ -247,6 +247,59 @@ int awq_gemm_noalloc(const uint16_t* x, const uint16_t* inv_s_c, const void* pac
                      hipStream_t stream);
 
 /*
+ * Decode chain: the M = 1 products of one decoder block in a single launch
+ * (edgesiliconlab ?p=2015, section "The Mathematics of Memory Bandwidth Saturation":
+ * at batch 1 a token costs the bytes of every weight it streams, so the time between
+ * products is lost bandwidth). Each layer i computes, as awq_gemv does at M = 1,
+ *   y_i[n] = binary16( sum_k X'_i[k] * (q_i[n][k] - z) * s ),  X'_i = binary16(in_i * inv_s_c_i),
+ * where in_i is the caller's x when src == -1 and layer src's output y_src otherwise
+ * (src < i: the layer starts once every output of layer src is written). Layers that
+ * do not depend on each other overlap; the weights of a layer are read while the
+ * layers before it finish. Within 2e-3 of the exact product of the dequantized
+ * weights with the layer's binary16 input, relative to max|y_i|; the same bits on
+ * every call.
+ */
+typedef struct awq_chain_layer {
+  const uint16_t* x;       /* device, [K] binary16; used when src == -1, else ignored */
+  const uint16_t* inv_s_c; /* device, [K] binary16, or NULL                         */
+  const void* packed;      /* device, gfx950 layout from awq_repack for (N, K, group, fmt) */
+  uint16_t* y;             /* device, [N] binary16, written                          */
+  int64_t N, K;
+  int32_t group, fmt;
+  int32_t src;             /* -1, or the index of an earlier layer whose N equals K  */
+  int32_t reserved;        /* set to 0                                               */
+} awq_chain_layer;
+
+/* Most layers one awq_gemv_chain call takes. */
+#define AWQ_CHAIN_MAX_LAYERS 8
+
+/*
+ * Bytes of the chain state buffer. The caller allocates it (device, 16-byte aligned),
+ * sets it to zero once before the first call, and passes the same buffer to every
+ * call; each call leaves it as it found it, except word 0 (uint32): bit 0 set means a
+ * wait inside a call ran out (about 0.17 s), and that call's outputs are not valid
+ * (clear the word, or the whole buffer, before the next call).
+ */
+size_t awq_chain_state_bytes(void);
+
+/*
+ * awq_gemv_chain - run `n_layers` M = 1 products in one launch, in the order given.
+ * layers  host array of n_layers descriptors (read during the call only).
+ * Shapes: as awq_gemv, and 1920 <= K <= 16384, group a multiple of 128 (per-channel
+ * included: AWQ_ERR_UNSUPPORTED otherwise). Each layer's y must be a buffer of its own,
+ * not read by any layer as x. n_layers == 0 returns AWQ_OK without launching;
+ * n_layers > AWQ_CHAIN_MAX_LAYERS is AWQ_ERR_UNSUPPORTED.
+ * state   device, awq_chain_state_bytes() bytes (see above). Calls that share a state
+ *         buffer must be ordered (same stream); a call uses every CU of the device and
+ *         waits inside the launch for its own earlier layers, so it must not share the
+ *         device with a kernel that waits for it.
+ * Errors: INVALID_ARG (NULL buffer, src out of range, input length != K),
+ *         UNSUPPORTED, MISALIGNED, HIP.
+ */
+int awq_gemv_chain(const awq_chain_layer* layers, int32_t n_layers, void* state,
+                   hipStream_t stream);
+
+/*
  * Workspace bytes awq_scale_search needs for (rows, N, K, group, fmt); 0 for arguments it
  * would reject.
  */

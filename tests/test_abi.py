@@ -30,7 +30,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(awq.EXPORTS) == names
@@ -68,6 +68,43 @@ def test_gemm_noalloc_checks_before_any_launch(lib):
     assert awq.awq_workspace_bytes(4096, 8192, 28672) > 64 << 20
     assert f(a, None, a, 4096, 8192, 28672, 128, 0, a, None) == WORKSPACE
     assert f(a, None, a, 0, 4096, 4096, 128, 0, a, None) == OK   # M = 0: no launch
+
+
+def test_chain_checks_before_any_launch(lib):
+    """awq_gemv_chain validates every layer descriptor before launching anything."""
+    f = lib.awq_gemv_chain
+    a = 1 << 20   # 16-byte aligned stand-in addresses (never dereferenced)
+    state = 1 << 24
+
+    def layers(*specs):
+        arr = (awq.ChainLayer * max(1, len(specs)))()
+        for i, sp in enumerate(specs):
+            d = dict(x=a, inv_s_c=None, packed=a, y=a + 4096 * (i + 1), N=4096, K=4096,
+                     group=128, fmt=0, src=-1, reserved=0)
+            d.update(sp)
+            arr[i] = awq.ChainLayer(**d)
+        return ctypes.cast(arr, ctypes.c_void_p)
+
+    ok = layers({}, {"src": 0, "x": None})
+    assert f(ok, 0, state, None) == OK                     # no layers: nothing to launch
+    assert f(None, 1, state, None) == INVALID
+    assert f(ok, 2, None, None) == INVALID
+    assert f(ok, -1, state, None) == INVALID
+    assert f(layers(*[{}] * 9), 9, state, None) == UNSUPPORTED   # more than 8 layers
+    assert f(layers({"x": None}), 1, state, None) == INVALID        # src -1 needs x
+    assert f(layers({"packed": None}), 1, state, None) == INVALID
+    assert f(layers({"y": None}), 1, state, None) == INVALID
+    assert f(layers({}, {"src": 1}), 2, state, None) == INVALID    # src must be earlier
+    assert f(layers({}, {"src": -2}), 2, state, None) == INVALID
+    assert f(layers({"N": 11008}, {"src": 0, "K": 4096}), 2, state, None) == INVALID  # N != K
+    assert f(layers({"N": 4100}), 1, state, None) == INVALID       # N % 8
+    assert f(layers({"group": 64}), 1, state, None) == UNSUPPORTED  # groups of 128 and up
+    assert f(layers({"K": 512, "x": a}), 1, state, None) == UNSUPPORTED   # K < 1024
+    assert f(layers({"K": 28672}), 1, state, None) == UNSUPPORTED  # K > 16384
+    assert f(layers({"x": a + 8}), 1, state, None) == MISALIGNED
+    assert f(layers({"inv_s_c": a + 2}), 1, state, None) == MISALIGNED
+    assert f(ok, 2, state + 4, None) == MISALIGNED
+    assert awq.awq_chain_state_bytes() > 0 and awq.awq_chain_state_bytes() % 256 == 0
 
 
 def test_status_strings(lib):
