@@ -298,8 +298,7 @@ def main():
         # ------------------------- the decoder block as one awq_gemv_chain launch (NEXT-2)
         # the seven products with the block's dependencies (q, k, v read x; o reads v;
         # gate and up read o; down reads up), one launch per step over rotating weights;
-        # beside it the same launch with every layer reading x (no waits inside), and both
-        # submitted eagerly (no graph) against seven eager awq_gemv launches
+        # beside it the same launch with every layer reading x (no waits inside)
         log("decoder block as one launch (awq_gemv_chain)")
         cl = [make_layer(1, n, k, layer=30 + j) for j, (_, n, k) in enumerate(DECODE_LAYERS)]
         c_bytes = sum(rl.algorithmic_bytes(1, L["n"], L["k"], GROUP, rl.FMT_ASYM, True) for L in cl)
@@ -318,32 +317,12 @@ def main():
             us = graph_us([(lambda sp=sp: awq.awq_gemv_chain(sp, state)) for sp in specs],
                           max(2, K // c_rot))
             res[tag] = {"us_per_step": round(us, 3), "GB/s": round(c_bytes / us / 1e3, 1)}
-            # eager submission through the Python binding, no graph: host cost included
-            torch.cuda.synchronize()
-            n_eager = max(20, K)
-            t0 = time.perf_counter()
-            for i in range(n_eager):
-                awq.awq_gemv_chain(specs[i % c_rot], state)
-            torch.cuda.synchronize()
-            res[tag]["eager_us_per_step"] = round((time.perf_counter() - t0) / n_eager * 1e6, 3)
-        ws = None
-        for L in cl:
-            ws = awq.workspace(1, L["n"], L["k"], dev)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(max(20, K)):
-            for j, L in enumerate(cl):
-                awq.awq_gemv(L["x"], L["inv"], c_cp[j][i % c_rot], L["n"], L["k"], GROUP,
-                             awq.FMT_ASYM, y=L["y"], ws=ws)
-        torch.cuda.synchronize()
-        sep_eager = (time.perf_counter() - t0) / max(20, K) * 1e6
         torch.cuda.synchronize()
         errors = awq.chain_errors(state)
         extra["chain_step"] = {
             "entry": "awq_gemv_chain", "launches_per_step": 1,
             "dependencies": "q, k, v <- x; o <- v; gate, up <- o; down <- up",
-            **res, "seven_launches_eager_us_per_step": round(sep_eager, 3),
-            "waits_timed_out": errors,
+            **res, "waits_timed_out": errors,
             "linear_tok_per_s_7b": round(1e6 / (N_BLOCKS_7B * res["block"]["us_per_step"]), 1)}
         del c_cp, cl, state
         torch.cuda.empty_cache()

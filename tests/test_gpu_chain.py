@@ -207,6 +207,7 @@ def test_chain_decoder_block_against_oracle(block):
         yy = y.cpu().numpy()
         assert np.all(np.isfinite(yy)), name
         err = rel_err(yy, r)
+        print(f"chain {name}: depth {d}, max|y - y_ref| / max|y_ref| = {err:.2e}")
         assert err <= TOL * (d + 1), (name, d, err)
 
 
