@@ -102,7 +102,7 @@ struct XPass {
 // compiler marks them for kernarg preloading: the command processor writes them into
 // SGPRs when it launches a wavefront, and the kernel starts without waiting for a load
 // of its argument block (0.3-0.4 us of a 4-7 us decode launch on MI355X).
-template <int M, int WAVES, int BATCH, bool ASYM, bool EXACT>
+template <int M, int WAVES, int BATCH, bool ASYM, bool EXACT, int T>
 __global__ void __launch_bounds__(WAVES * 64)
     gemv_kernel(const uint16_t* x, const uint16_t* inv, const uint8_t* packed, uint16_t* y,
                 uint32_t scales_off, uint32_t zeros_off, int N, int K, int phase_groups, int n_sets) {
@@ -120,7 +120,11 @@ __global__ void __launch_bounds__(WAVES * 64)
   a.sets = n_sets;
   constexpr int JM = M < 4 ? M : 4;  // D rows per lane that can be real rows
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int t = blockIdx.x;
+  // T > 1: the workgroup takes T consecutive 16-row tiles (every wavefront's staged X'
+  // then serves T weight tiles); a tile past the last one reads the last one again and
+  // stores nothing (its rows are >= N)
+  const int t0 = blockIdx.x * T;
+  const int n_tiles = (a.N + kTileN - 1) / kTileN;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, p = lane >> 4;
@@ -132,16 +136,18 @@ __global__ void __launch_bounds__(WAVES * 64)
   _Float16* xs = reinterpret_cast<_Float16*>(smem);        // [M][PK]
   float* osum = reinterpret_cast<float*>(smem + 2 * M * PK);  // [M][PG]
   float* ssum = osum + M * PG;                               // [M][PG]
-  float* red = ssum + M * PG;                                // [WAVES][M][16]
+  float* red = ssum + M * PG;                                // [WAVES][M][T * 16]
 
-  const __amdgpu_buffer_rsrc_t rcodes =
-      make_rsrc(a.packed + static_cast<int64_t>(t) * ng * kUnitBytes, ng * kUnitBytes);
   const int sets = a.sets;
   const uint32_t sbytes = 2 * kTileN * sets, zbytes = 8 * sets;  // per unit
-  const __amdgpu_buffer_rsrc_t rscales =
-      make_rsrc(a.packed + a.scales_off + static_cast<int64_t>(t) * ng * sbytes, ng * sbytes);
-  const __amdgpu_buffer_rsrc_t rzeros =
-      make_rsrc(a.packed + (ASYM ? a.zeros_off : 0) + static_cast<int64_t>(t) * ng * zbytes, ng * zbytes);
+  __amdgpu_buffer_rsrc_t rcodes[T], rscales[T], rzeros[T];
+#pragma unroll
+  for (int j = 0; j < T; ++j) {
+    const int64_t t = T == 1 ? t0 : min(t0 + j, n_tiles - 1);
+    rcodes[j] = make_rsrc(a.packed + t * ng * kUnitBytes, ng * kUnitBytes);
+    rscales[j] = make_rsrc(a.packed + a.scales_off + t * ng * sbytes, ng * sbytes);
+    rzeros[j] = make_rsrc(a.packed + (ASYM ? a.zeros_off : 0) + t * ng * zbytes, ng * zbytes);
+  }
   const int lset = lane_set(p, sets);
   const uint32_t lane_code = 16u * lane, lane_scale = 2u * (kTileN * lset + r),
                  lane_zero = 4u * (2 * lset + (r >> 3));
@@ -152,14 +158,18 @@ __global__ void __launch_bounds__(WAVES * 64)
   const uint4 ones = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
   const int arow = r < M ? r : M - 1;
 
-  float yacc[JM];
+  float yacc[T][JM];
 #pragma unroll
-  for (int j = 0; j < JM; ++j) yacc[j] = 0.0f;
-  float4_t dacc = {0.0f, 0.0f, 0.0f, 0.0f};  // EXACT: sum over groups of X' W_d
+  for (int tj = 0; tj < T; ++tj)
+#pragma unroll
+    for (int j = 0; j < JM; ++j) yacc[tj][j] = 0.0f;
+  float4_t dacc[T];  // EXACT: sum over groups of X' W_d
+#pragma unroll
+  for (int tj = 0; tj < T; ++tj) dacc[tj] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   struct Batch {
-    uint4 c[BATCH];
-    uint32_t s[BATCH], z[BATCH];
+    uint4 c[BATCH][T];
+    uint32_t s[BATCH][T], z[BATCH][T];
   };
   // groups gl = wave + WAVES * j of the phase, j < nj; a slot past nj loads nothing
   auto load = [&](Batch& b, int ph0, int jb, int nj) {
@@ -168,9 +178,12 @@ __global__ void __launch_bounds__(WAVES * 64)
       const bool live = jb + u < nj;
       const uint32_t g = live ? static_cast<uint32_t>(ph0 + wave + WAVES * (jb + u)) : 0u;
       const uint32_t skip = live ? 0u : kNoLoad;
-      b.c[u] = buf_load16_stream(rcodes, lane_code + skip, g * kUnitBytes);
-      b.s[u] = buf_load2(rscales, lane_scale + skip, g * sbytes);
-      if (ASYM) b.z[u] = buf_load4(rzeros, lane_zero + skip, g * zbytes);
+#pragma unroll
+      for (int tj = 0; tj < T; ++tj) {
+        b.c[u][tj] = buf_load16_stream(rcodes[tj], lane_code + skip, g * kUnitBytes);
+        b.s[u][tj] = buf_load2(rscales[tj], lane_scale + skip, g * sbytes);
+        if (ASYM) b.z[u][tj] = buf_load4(rzeros[tj], lane_zero + skip, g * zbytes);
+      }
     }
   };
   auto compute = [&](const Batch& b, int jb, int nj) {
@@ -179,36 +192,49 @@ __global__ void __launch_bounds__(WAVES * 64)
       if (jb + u < nj) {
         const int gl = wave + WAVES * (jb + u);
         const _Float16* xg = xs + arow * PK + gl * kGroup + 32 * p;
-        const uint32_t words[4] = {b.c[u].x, b.c[u].y, b.c[u].z, b.c[u].w};
         if constexpr (EXACT) {
-          const uint32_t z = ASYM ? (b.z[u] >> zshift) & 0xFu : 8u;
-          const half2_t s2 = as_h2(b.s[u] | (b.s[u] << 16));
-          const uint32_t nz1024 = neg_off1024(z), nz64 = neg_off64(z);
+          half2_t s2[T];
+          uint32_t nz1024[T], nz64[T];
+#pragma unroll
+          for (int tj = 0; tj < T; ++tj) {
+            const uint32_t z = ASYM ? (b.z[u][tj] >> zshift) & 0xFu : 8u;
+            s2[tj] = as_h2(b.s[u][tj] | (b.s[u][tj] << 16));
+            nz1024[tj] = neg_off1024(z);
+            nz64[tj] = neg_off64(z);
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            half2_t dq[4];
-            dequant_word(words[i], nz1024, nz64, s2, dq);
-            const half8_t bf = {dq[0].x, dq[0].y, dq[1].x, dq[1].y, dq[2].x, dq[2].y, dq[3].x, dq[3].y};
             const half8_t af = *reinterpret_cast<const half8_t*>(xg + 8 * i);
-            dacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, dacc, 0, 0, 0);
+#pragma unroll
+            for (int tj = 0; tj < T; ++tj) {
+              const uint32_t w = i == 0 ? b.c[u][tj].x : i == 1 ? b.c[u][tj].y : i == 2 ? b.c[u][tj].z : b.c[u][tj].w;
+              half2_t dq[4];
+              dequant_word(w, nz1024[tj], nz64[tj], s2[tj], dq);
+              const half8_t bf = {dq[0].x, dq[0].y, dq[1].x, dq[1].y, dq[2].x, dq[2].y, dq[3].x, dq[3].y};
+              dacc[tj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, dacc[tj], 0, 0, 0);
+            }
           }
           continue;
         }
-        float4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const Pairs4 pr = unpack_word_mfma(words[i]);
-          const u32x4_t bw = {pr.p[0], pr.p[1], pr.p[2], pr.p[3]};
-          const half8_t af = *reinterpret_cast<const half8_t*>(xg + 8 * i);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, __builtin_bit_cast(half8_t, bw), d, 0, 0, 0);
-        }
-        const float s = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b.s[u])));
-        const float z = ASYM ? static_cast<float>((b.z[u] >> zshift) & 0xFu) : 8.0f;
+        for (int tj = 0; tj < T; ++tj) {
+          const uint32_t words[4] = {b.c[u][tj].x, b.c[u][tj].y, b.c[u][tj].z, b.c[u][tj].w};
+          float4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int j = 0; j < JM; ++j) {
-          const int m = min(4 * p + j, M - 1);
-          const int e = m * PG + gl;
-          yacc[j] += s * (d[j] - osum[e] - z * ssum[e]);
+          for (int i = 0; i < 4; ++i) {
+            const Pairs4 pr = unpack_word_mfma(words[i]);
+            const u32x4_t bw = {pr.p[0], pr.p[1], pr.p[2], pr.p[3]};
+            const half8_t af = *reinterpret_cast<const half8_t*>(xg + 8 * i);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, __builtin_bit_cast(half8_t, bw), d, 0, 0, 0);
+          }
+          const float s = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b.s[u][tj])));
+          const float z = ASYM ? static_cast<float>((b.z[u][tj] >> zshift) & 0xFu) : 8.0f;
+#pragma unroll
+          for (int j = 0; j < JM; ++j) {
+            const int m = min(4 * p + j, M - 1);
+            const int e = m * PG + gl;
+            yacc[tj][j] += s * (d[j] - osum[e] - z * ssum[e]);
+          }
         }
       }
     }
@@ -286,69 +312,100 @@ __global__ void __launch_bounds__(WAVES * 64)
 
   if constexpr (EXACT) {
 #pragma unroll
-    for (int j = 0; j < JM; ++j) yacc[j] = dacc[j];
+    for (int tj = 0; tj < T; ++tj)
+#pragma unroll
+      for (int j = 0; j < JM; ++j) yacc[tj][j] = dacc[tj][j];
   }
   // the wavefronts' partial sums through LDS; one thread per (row, output) writes y
+  constexpr int TN = T * kTileN;
 #pragma unroll
-  for (int j = 0; j < JM; ++j) {
-    const int m = 4 * p + j;
-    if (m < M) red[(wave * M + m) * kTileN + r] = yacc[j];
-  }
+  for (int tj = 0; tj < T; ++tj)
+#pragma unroll
+    for (int j = 0; j < JM; ++j) {
+      const int m = 4 * p + j;
+      if (m < M) red[(wave * M + m) * TN + tj * kTileN + r] = yacc[tj][j];
+    }
   __syncthreads();
-  if (threadIdx.x < M * kTileN) {
-    const int m = threadIdx.x / kTileN, rr = threadIdx.x % kTileN;
-    float v = red[m * kTileN + rr];
+  for (int i = threadIdx.x; i < M * TN; i += WAVES * 64) {
+    const int m = i / TN, c = i % TN;
+    float v = red[m * TN + c];
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) v += red[(w * M + m) * kTileN + rr];
-    const int n = t * kTileN + rr;
+    for (int w = 1; w < WAVES; ++w) v += red[(w * M + m) * TN + c];
+    const int n = t0 * kTileN + c;
     if (n < a.N) {
       a.y[static_cast<int64_t>(m) * a.N + n] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
     }
   }
 }
 
-int phase_groups_for(int M, int n_groups, int64_t n_tiles) {
-  const int budget = n_tiles <= 256 ? kLdsAlone : kLdsShared;
+// X' phase length (groups staged at once). One workgroup per tile (T = 1): 144 KiB of LDS
+// when at most one workgroup runs per CU (n_tiles <= 256), else 60 KiB (two fit beside
+// each other). With T tiles per workgroup the same two cases, less the partial-sum area.
+int phase_groups_for(int M, int n_groups, int64_t n_tiles, int T, int waves) {
+  const int64_t wgs = (n_tiles + T - 1) / T;
+  int budget;
+  if (T == 1) {
+    budget = n_tiles <= 256 ? kLdsAlone : kLdsShared;
+  } else {
+    budget = (wgs <= 256 ? 163840 : 81920) - 4 * waves * M * kTileN * T - 1024;
+  }
   int pg = budget / (M * (2 * kGroup + 8));
   if (pg > n_groups) pg = n_groups;
   return pg < 1 ? 1 : pg;
 }
 
-size_t smem_bytes(int M, int phase_groups, int waves) {
+size_t smem_bytes(int M, int phase_groups, int waves, int T) {
   return static_cast<size_t>(2) * M * phase_groups * kGroup + 8ull * M * phase_groups +
-         4ull * waves * M * kTileN;
+         4ull * waves * M * kTileN * T;
 }
 
-template <int M, int WAVES, int BATCH, bool ASYM, bool EXACT>
+template <int M, int WAVES, int BATCH, bool ASYM, bool EXACT, int T>
 hipError_t launch_fmt(const MvArgs& a, int64_t n_tiles, hipStream_t st) {
-  const size_t lds = smem_bytes(M, a.phase_groups, WAVES);
+  const size_t lds = smem_bytes(M, a.phase_groups, WAVES, T);
   static std::atomic<uint64_t> lds_done{0};
   const hipError_t ea = ensure_lds_limit(
-      reinterpret_cast<const void*>(&gemv_kernel<M, WAVES, BATCH, ASYM, EXACT>),
-      kLdsAlone + 4 * WAVES * M * kTileN, lds_done);
+      reinterpret_cast<const void*>(&gemv_kernel<M, WAVES, BATCH, ASYM, EXACT, T>), 163840, lds_done);
   if (ea != hipSuccess) return ea;
-  hipLaunchKernelGGL((gemv_kernel<M, WAVES, BATCH, ASYM, EXACT>), dim3(static_cast<unsigned>(n_tiles)),
-                     dim3(WAVES * 64), lds, st, a.x, a.inv, a.packed, a.y,
-                     static_cast<uint32_t>(a.scales_off), static_cast<uint32_t>(ASYM ? a.zeros_off : 0),
-                     a.N, a.K, a.phase_groups, a.sets);
+  hipLaunchKernelGGL((gemv_kernel<M, WAVES, BATCH, ASYM, EXACT, T>),
+                     dim3(static_cast<unsigned>((n_tiles + T - 1) / T)), dim3(WAVES * 64), lds, st,
+                     a.x, a.inv, a.packed, a.y, static_cast<uint32_t>(a.scales_off),
+                     static_cast<uint32_t>(ASYM ? a.zeros_off : 0), a.N, a.K, a.phase_groups, a.sets);
   return hipGetLastError();
 }
 
 // The per-group correction needs the activation sums O and S of every row: from five
 // rows on, staging them costs more than dequantizing each weight exactly, so M > 4 (and
 // groups of 32 or 64) take the exact form.
-template <int M, int WAVES, int BATCH>
+template <int M, int WAVES, int BATCH, int T = 1>
 hipError_t launch_cfg(const MvArgs& a, int64_t n_tiles, hipStream_t st) {
   const bool asym = a.zeros_off >= 0;
   if (M > 4 || a.sets > 1) {
-    return asym ? launch_fmt<M, WAVES, BATCH, true, true>(a, n_tiles, st)
-                : launch_fmt<M, WAVES, BATCH, false, true>(a, n_tiles, st);
+    return asym ? launch_fmt<M, WAVES, BATCH, true, true, T>(a, n_tiles, st)
+                : launch_fmt<M, WAVES, BATCH, false, true, T>(a, n_tiles, st);
   }
   if constexpr (M <= 4) {
-    return asym ? launch_fmt<M, WAVES, BATCH, true, false>(a, n_tiles, st)
-                : launch_fmt<M, WAVES, BATCH, false, false>(a, n_tiles, st);
+    return asym ? launch_fmt<M, WAVES, BATCH, true, false, T>(a, n_tiles, st)
+                : launch_fmt<M, WAVES, BATCH, false, false, T>(a, n_tiles, st);
   }
   return hipErrorInvalidValue;
+}
+
+// Tiles per workgroup at M > 4, where each wavefront stages the activations of every
+// row for its groups: with T tiles per workgroup that staging serves T weight tiles.
+// From a sweep of T = 1, 2, 4 at M = 5 .. 16 on 4096 -> 11008, 11008 -> 4096 and the
+// 70B layers (MI355X): two tiles from 512 row tiles on (4096 -> 11008 at M = 8: 10.0
+// instead of 13.0 us; 28672 -> 8192 at M = 16: 45 instead of 78 us), four from M = 12 on
+// when that still leaves 160 workgroups or more (8192 -> 28672 at M = 16: 50 instead of
+// 89 us); fewer rows or tiles stay at one. (awq_gemm's split-K tiles are faster still on
+// these shapes and are what it runs.) Tuning builds: AWQ_GEMV_T forces 1, 2 or 4.
+int tiles_per_wg(int M, int64_t n_tiles) {
+  if (const char* env = tuning_env("AWQ_GEMV_T")) {
+    const int t = atoi(env);
+    if (t == 1 || t == 2 || t == 4) return t;
+  }
+  if (M <= 4 || n_tiles < 512) return 1;
+  if (M >= 12 && n_tiles >= 640) return 4;
+  return 2;
 }
 
 // From sweeps on MI355X (4096 <= K, N <= 28672): long rows on few tiles (K >= 8192,
@@ -356,10 +413,18 @@ hipError_t launch_cfg(const MvArgs& a, int64_t n_tiles, hipStream_t st) {
 // flight each; everything else eight wavefronts with one group each. Sixteen
 // wavefronts leave 128 VGPRs per lane, which the staging of more than four activation
 // rows overflows (spills to scratch), so M > 4 always takes eight.
+int waves_for(int M, int n_groups, int64_t n_tiles) {
+  return M <= 4 && n_groups >= 64 && n_tiles <= 512 ? 16 : 8;
+}
+
 template <int M>
-hipError_t launch_m(const MvArgs& a, int64_t n_tiles, hipStream_t st) {
+hipError_t launch_m(const MvArgs& a, int64_t n_tiles, int T, hipStream_t st) {
   if constexpr (M <= 4) {
-    if (a.n_groups >= 64 && n_tiles <= 512) return launch_cfg<M, 16, 1>(a, n_tiles, st);
+    if (waves_for(M, a.n_groups, n_tiles) == 16) return launch_cfg<M, 16, 1>(a, n_tiles, st);
+  }
+  if constexpr (M > 4) {
+    if (T == 4) return launch_cfg<M, 8, 1, 4>(a, n_tiles, st);
+    if (T == 2) return launch_cfg<M, 8, 1, 2>(a, n_tiles, st);
   }
   return launch_cfg<M, 8, 1>(a, n_tiles, st);
 }
@@ -380,7 +445,7 @@ hipError_t launch_m1(const MvArgs& a, int64_t n_tiles, hipStream_t st) {
     case 82: return launch_cfg<1, 8, 2>(a, n_tiles, st);
     case 161: return launch_cfg<1, 16, 1>(a, n_tiles, st);
     case 162: return launch_cfg<1, 16, 2>(a, n_tiles, st);
-    default: return launch_m<1>(a, n_tiles, st);
+    default: return launch_m<1>(a, n_tiles, 1, st);
   }
 }
 
@@ -403,24 +468,26 @@ hipError_t launch_gemv(const uint16_t* x, const uint16_t* inv_s_c, const void* p
   a.K = static_cast<int>(K);
   a.n_groups = static_cast<int>(L.n_groups);
   a.sets = static_cast<int>(L.sets);
-  a.phase_groups = phase_groups_for(static_cast<int>(M), a.n_groups, L.n_tiles);
+  const int T = tiles_per_wg(static_cast<int>(M), L.n_tiles);
+  a.phase_groups = phase_groups_for(static_cast<int>(M), a.n_groups, L.n_tiles, T,
+                                    T == 1 ? waves_for(static_cast<int>(M), a.n_groups, L.n_tiles) : 8);
   switch (M) {
     case 1: return launch_m1(a, L.n_tiles, st);
-    case 2: return launch_m<2>(a, L.n_tiles, st);
-    case 3: return launch_m<3>(a, L.n_tiles, st);
-    case 4: return launch_m<4>(a, L.n_tiles, st);
-    case 5: return launch_m<5>(a, L.n_tiles, st);
-    case 6: return launch_m<6>(a, L.n_tiles, st);
-    case 7: return launch_m<7>(a, L.n_tiles, st);
-    case 8: return launch_m<8>(a, L.n_tiles, st);
-    case 9: return launch_m<9>(a, L.n_tiles, st);
-    case 10: return launch_m<10>(a, L.n_tiles, st);
-    case 11: return launch_m<11>(a, L.n_tiles, st);
-    case 12: return launch_m<12>(a, L.n_tiles, st);
-    case 13: return launch_m<13>(a, L.n_tiles, st);
-    case 14: return launch_m<14>(a, L.n_tiles, st);
-    case 15: return launch_m<15>(a, L.n_tiles, st);
-    case 16: return launch_m<16>(a, L.n_tiles, st);
+    case 2: return launch_m<2>(a, L.n_tiles, 1, st);
+    case 3: return launch_m<3>(a, L.n_tiles, 1, st);
+    case 4: return launch_m<4>(a, L.n_tiles, 1, st);
+    case 5: return launch_m<5>(a, L.n_tiles, T, st);
+    case 6: return launch_m<6>(a, L.n_tiles, T, st);
+    case 7: return launch_m<7>(a, L.n_tiles, T, st);
+    case 8: return launch_m<8>(a, L.n_tiles, T, st);
+    case 9: return launch_m<9>(a, L.n_tiles, T, st);
+    case 10: return launch_m<10>(a, L.n_tiles, T, st);
+    case 11: return launch_m<11>(a, L.n_tiles, T, st);
+    case 12: return launch_m<12>(a, L.n_tiles, T, st);
+    case 13: return launch_m<13>(a, L.n_tiles, T, st);
+    case 14: return launch_m<14>(a, L.n_tiles, T, st);
+    case 15: return launch_m<15>(a, L.n_tiles, T, st);
+    case 16: return launch_m<16>(a, L.n_tiles, T, st);
     default: return hipErrorInvalidValue;
   }
 }

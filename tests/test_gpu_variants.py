@@ -111,6 +111,23 @@ def test_decode_correction_form_many_phases(m, fmt):
     L.check(awq.awq_gemv(to_dev(L.x), L.inv, L.packed, n, k, 128, fmt))
 
 
+# awq_gemv at M > 4 on layers of 512 row tiles or more takes two or four 16-row tiles per
+# workgroup (one staging of the activations serves all of them). Ragged cases: 513 and 641
+# row tiles (the last tile half full), so the last workgroup's later tiles lie past N.
+MULTI_TILE_CASES = [
+    ("t2_ragged_asym_m8", 8200, 1024, 8, 0),     # 513 tiles, 2 per workgroup
+    ("t2_sym_m5", 8192, 2048, 5, 1),             # 512 tiles, 2 per workgroup
+    ("t4_ragged_sym_m12", 10248, 1024, 12, 1),   # 641 tiles, 4 per workgroup
+    ("t4_asym_m16_long", 10240, 3072, 16, 0),    # 640 tiles, 4 per workgroup, 24 groups
+]
+
+
+@pytest.mark.parametrize("name,n,k,m,fmt", MULTI_TILE_CASES, ids=[c[0] for c in MULTI_TILE_CASES])
+def test_gemv_several_tiles_per_workgroup(name, n, k, m, fmt):
+    L = Layer(n, k, m, fmt, config=6, rows=np.arange(n))
+    L.check(awq.awq_gemv(to_dev(L.x), L.inv, L.packed, n, k, 128, fmt))
+
+
 # ----------------------------------------------------------- awq_gemm narrow tilings
 
 # M = 48 on a layer of more than 2^26 weights: 64 x 128 workgroup tiles, K split;
