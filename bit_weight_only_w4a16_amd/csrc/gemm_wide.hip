@@ -75,7 +75,16 @@ __global__ void __launch_bounds__(256 * KS) gemm_wide_kernel(WideArgs a) {
 
   const int nb = a.n_blocks_m * a.n_blocks_n;
   const int bid = xcd_block(blockIdx.x, nb);
-  const int bm = bid % a.n_blocks_m, bn = bid / a.n_blocks_m;
+  // output blocks in bands of 8 row blocks, row block fastest within a band: the ~64
+  // workgroups resident on one XCD at a time (consecutive block numbers) then cover about
+  // 8 row blocks x 8 column blocks, so its L2 holds fewer distinct X' rows and weight
+  // columns than with all row blocks x a few column blocks (measured: 1.5-3.5 % faster
+  // on the Llama-3-8B prefill shapes)
+  const int per_band = 8 * a.n_blocks_n;
+  const int band = bid / per_band;
+  const int rows_in = min(8, a.n_blocks_m - band * 8);
+  const int lb = bid - band * per_band;
+  const int bm = band * 8 + lb % rows_in, bn = lb / rows_in;
   const int m_blk = bm * kBM, n_blk = bn * BN;
   const int ng = a.n_groups;
   // this workgroup's units [ga, gb) (split blockIdx.y of K), then this wavefront's
