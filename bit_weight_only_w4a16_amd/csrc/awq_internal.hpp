@@ -110,6 +110,10 @@ hipError_t launch_dequant_packed(const void* packed, int64_t N, int64_t K, int32
                                  int32_t fmt, uint16_t* w_out, hipStream_t st);
 
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// The decode kernel's row tiles per workgroup and its number of X' staging phases for an
+// M x N x K product (1 <= M <= 16)
+int gemv_tiles_per_wg(int64_t M, int64_t N);
+int gemv_phases(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
                        int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt, uint16_t* y,
                        void* ws, size_t ws_bytes, hipStream_t st);

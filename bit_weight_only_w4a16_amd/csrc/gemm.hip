@@ -461,19 +461,32 @@ hipError_t launch_splitk_reduce(const float* part, int splits, int64_t mn, uint1
   }
 }
 
-// Where the decode kernel (one workgroup per 16-row tile and all of K: no split, no second
-// launch, no workspace) is faster than the split-K tiles (measured on MI355X, 4096 <= K, N
-// <= 28672): always at M <= 2 (4096 -> 11008: 6.5 / 7.3 instead of 10.2 / 10.4 us; the
-// 70B layers: 21.6 / 24.3 instead of 28.0 / 27.8 us); at M <= 4 on layers of at most 2^15
-// 16 x 128 units (4096 -> 11008 at M = 4: 9.4 instead of 10.6 us; on the 70B layers it is
-// slower); and up to 16 rows on layers of at most 256 row tiles while the staged
-// activations of its groups fit in LDS in about one pass (4096 -> 4096 at M = 8, 5.3
-// instead of 8.2 us; 11008 -> 4096 at M = 8, 11.4 instead of 12.7 us).
+// Where the decode kernel (whole 16-row tiles and all of K per workgroup: no split, no
+// second launch, no workspace) is faster than the split-K tiles (measured on MI355X, 4096
+// <= K, N <= 28672): always at M <= 2 (4096 -> 11008: 6.5 / 7.0 instead of 10.2 / 10.4
+// us; the 70B layers: 21.6 / 23.5 instead of 28.0 / 27.8 us); at M <= 4 on layers of at
+// most 2^15 16 x 128 units (4096 -> 11008 at M = 4: 7.5 instead of 10.6 us) or of more than
+// 512 row tiles (two tiles per workgroup there: 4096 -> 22016 / 8192 -> 28672 at M = 3,
+// 11.7 / 25.3 instead of 14.5 / 27.4 us; with 512 tiles or fewer and long rows it runs
+// sixteen wavefronts per tile, and 28672 -> 8192 at M = 3 / 4 takes 31 / 35 us there
+// against 29 / 29 us for the split-K tiles); up to 16 rows
+// on layers of at most 256 row tiles while the staged activations of its groups fit in
+// LDS in about one pass (4096 -> 4096 at M = 8, 5.3 instead of 8.2 us; 11008 -> 4096 at
+// M = 8, 11.4 instead of 12.7 us); and up to 16 rows on 257 .. 768 row tiles, where it
+// runs one workgroup of two or three tiles per CU, when the activations fit in one pass
+// (two for two tiles and K <= 8192): 4096 -> 6144 / 8192 / 11008 / 12288 at M = 8 6.5 /
+// 6.7 / 8.6 / 8.7 instead of 9.3 / 9.4 / 9.5 / 9.6 us, 8192 -> 8192 at M = 16 14.2
+// instead of 15.2 us; with more phases (5120 -> 12288 at M = 16, 28672 -> 8192 at M >= 5)
+// the split-K tiles stay faster.
 static bool small_m_takes_decode_kernel(int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = (N + kTileN - 1) / kTileN, groups = K / kGroup;
   if (M <= 2) return true;
-  if (M <= 4 && tiles * groups <= (int64_t{1} << 15)) return true;
-  return M <= 16 && tiles <= 256 && M * groups <= 704;
+  if (M <= 4 && (tiles * groups <= (int64_t{1} << 15) || tiles > 512)) return true;
+  if (M > 16) return false;
+  if (tiles <= 256) return M * groups <= 704;
+  if (tiles > 768) return false;
+  const int phases = gemv_phases(M, N, K);
+  return phases == 1 || (gemv_tiles_per_wg(M, N) == 2 && phases == 2 && groups <= 64);
 }
 
 // Large M runs the wide-tile kernel, which needs X' in the workspace when inv_s_c is

@@ -390,22 +390,24 @@ hipError_t launch_cfg(const MvArgs& a, int64_t n_tiles, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
-// Tiles per workgroup at M > 4, where each wavefront stages the activations of every
-// row for its groups: with T tiles per workgroup that staging serves T weight tiles.
-// From a sweep of T = 1, 2, 4 at M = 5 .. 16 on 4096 -> 11008, 11008 -> 4096 and the
-// 70B layers (MI355X): two tiles from 512 row tiles on (4096 -> 11008 at M = 8: 10.0
-// instead of 13.0 us; 28672 -> 8192 at M = 16: 45 instead of 78 us), four from M = 12 on
-// when that still leaves 160 workgroups or more (8192 -> 28672 at M = 16: 50 instead of
-// 89 us); fewer rows or tiles stay at one. (awq_gemm's split-K tiles are faster still on
-// these shapes and are what it runs.) Tuning builds: AWQ_GEMV_T forces 1, 2 or 4.
+// Tiles per workgroup at M >= 2. Each wavefront stages the activations of every row for
+// its groups, and with T tiles per workgroup that staging serves T weight tiles; a
+// workgroup's time also grows with its share of a CU. From sweeps of T = 1 .. 4 at
+// M = 1 .. 16 on K = 4096 with 256 .. 1792 row tiles and on the 70B layers (MI355X): up
+// to 768 tiles, T = ceil(tiles / 256), one workgroup per CU (4096 -> 11008 at M = 2 / 4 /
+// 8 / 16: 7.0 / 7.5 / 8.6 / 9.4 us against 8.6 / 9.6 / 13.1 / 21.6 with one tile); beyond
+// that two tiles, four from M = 12 (8192 -> 28672 at M = 2 / 16: 23.5 / 50 instead of
+// 28.2 / 89 us). At M = 1 the differences stayed within the run-to-run spread (4096 ->
+// 11008: 6.47 / 6.45 us with one / three tiles), and the tuned one-tile launch is kept.
+// Tuning builds: AWQ_GEMV_T forces 1 .. 4.
 int tiles_per_wg(int M, int64_t n_tiles) {
   if (const char* env = tuning_env("AWQ_GEMV_T")) {
     const int t = atoi(env);
-    if (t == 1 || t == 2 || t == 4) return t;
+    if (t >= 1 && t <= 4) return t;
   }
-  if (M <= 4 || n_tiles < 512) return 1;
-  if (M >= 12 && n_tiles >= 640) return 4;
-  return 2;
+  if (M == 1 || n_tiles <= 256) return 1;
+  if (n_tiles <= 768) return static_cast<int>((n_tiles + 255) / 256);
+  return M >= 12 ? 4 : 2;
 }
 
 // From sweeps on MI355X (4096 <= K, N <= 28672): long rows on few tiles (K >= 8192,
@@ -422,16 +424,15 @@ hipError_t launch_m(const MvArgs& a, int64_t n_tiles, int T, hipStream_t st) {
   if constexpr (M <= 4) {
     if (waves_for(M, a.n_groups, n_tiles) == 16) return launch_cfg<M, 16, 1>(a, n_tiles, st);
   }
-  if constexpr (M > 4) {
-    if (T == 4) return launch_cfg<M, 8, 1, 4>(a, n_tiles, st);
-    if (T == 2) return launch_cfg<M, 8, 1, 2>(a, n_tiles, st);
-  }
+  if (T == 4) return launch_cfg<M, 8, 1, 4>(a, n_tiles, st);
+  if (T == 3) return launch_cfg<M, 8, 1, 3>(a, n_tiles, st);
+  if (T == 2) return launch_cfg<M, 8, 1, 2>(a, n_tiles, st);
   return launch_cfg<M, 8, 1>(a, n_tiles, st);
 }
 
 // Tuning override for sweeps (M = 1 only, libraries built for tuning): AWQ_GEMV_CFG =
 // "waves,batch".
-hipError_t launch_m1(const MvArgs& a, int64_t n_tiles, hipStream_t st) {
+hipError_t launch_m1(const MvArgs& a, int64_t n_tiles, int T, hipStream_t st) {
   int cfg = 0;
   if (const char* env = tuning_env("AWQ_GEMV_CFG")) {
     int w = 0, b = 0;
@@ -445,13 +446,26 @@ hipError_t launch_m1(const MvArgs& a, int64_t n_tiles, hipStream_t st) {
     case 82: return launch_cfg<1, 8, 2>(a, n_tiles, st);
     case 161: return launch_cfg<1, 16, 1>(a, n_tiles, st);
     case 162: return launch_cfg<1, 16, 2>(a, n_tiles, st);
-    default: return launch_m<1>(a, n_tiles, 1, st);
+    default: return launch_m<1>(a, n_tiles, T, st);
   }
 }
 
 }  // namespace
 
 size_t gemv_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+
+int gemv_tiles_per_wg(int64_t M, int64_t N) {
+  return tiles_per_wg(static_cast<int>(M), (N + kTileN - 1) / kTileN);
+}
+
+int gemv_phases(int64_t M, int64_t N, int64_t K) {
+  const int64_t n_tiles = (N + kTileN - 1) / kTileN;
+  const int ng = static_cast<int>(K / kGroup);
+  const int T = tiles_per_wg(static_cast<int>(M), n_tiles);
+  const int pg = phase_groups_for(static_cast<int>(M), ng, n_tiles, T,
+                                  T == 1 ? waves_for(static_cast<int>(M), ng, n_tiles) : 8);
+  return (ng + pg - 1) / pg;
+}
 
 hipError_t launch_gemv(const uint16_t* x, const uint16_t* inv_s_c, const void* packed,
                        int64_t M, int64_t N, int64_t K, int32_t group, int32_t fmt, uint16_t* y,
@@ -472,10 +486,10 @@ hipError_t launch_gemv(const uint16_t* x, const uint16_t* inv_s_c, const void* p
   a.phase_groups = phase_groups_for(static_cast<int>(M), a.n_groups, L.n_tiles, T,
                                     T == 1 ? waves_for(static_cast<int>(M), a.n_groups, L.n_tiles) : 8);
   switch (M) {
-    case 1: return launch_m1(a, L.n_tiles, st);
-    case 2: return launch_m<2>(a, L.n_tiles, 1, st);
-    case 3: return launch_m<3>(a, L.n_tiles, 1, st);
-    case 4: return launch_m<4>(a, L.n_tiles, 1, st);
+    case 1: return launch_m1(a, L.n_tiles, T, st);
+    case 2: return launch_m<2>(a, L.n_tiles, T, st);
+    case 3: return launch_m<3>(a, L.n_tiles, T, st);
+    case 4: return launch_m<4>(a, L.n_tiles, T, st);
     case 5: return launch_m<5>(a, L.n_tiles, T, st);
     case 6: return launch_m<6>(a, L.n_tiles, T, st);
     case 7: return launch_m<7>(a, L.n_tiles, T, st);

@@ -115,17 +115,27 @@ def test_decode_correction_form_many_phases(m, fmt):
 # workgroup (one staging of the activations serves all of them). Ragged cases: 513 and 641
 # row tiles (the last tile half full), so the last workgroup's later tiles lie past N.
 MULTI_TILE_CASES = [
-    ("t2_ragged_asym_m8", 8200, 1024, 8, 0),     # 513 tiles, 2 per workgroup
+    # (name, N, K, M, fmt): T = ceil(tiles / 256) up to 768 row tiles, then 2 (4 from M = 12)
+    ("t2_ragged_asym_m8", 6152, 1024, 8, 0),     # 385 tiles, 2 per workgroup, last one alone
     ("t2_sym_m5", 8192, 2048, 5, 1),             # 512 tiles, 2 per workgroup
-    ("t4_ragged_sym_m12", 10248, 1024, 12, 1),   # 641 tiles, 4 per workgroup
-    ("t4_asym_m16_long", 10240, 3072, 16, 0),    # 640 tiles, 4 per workgroup, 24 groups
+    ("t3_ragged_sym_m12", 10248, 1024, 12, 1),   # 641 tiles, 3 per workgroup
+    ("t3_asym_m16_long", 10240, 3072, 16, 0),    # 640 tiles, 3 per workgroup, 24 groups
+    ("t3_ragged_asym_m3_corr", 11008, 1024, 3, 0),  # 688 tiles: the correction form, 3 tiles
+    ("t3_sym_m2_corr", 12288, 2048, 2, 1),       # 768 tiles: the correction form, 3 tiles
+    ("t2_ragged_sym_m4_corr", 12304, 1024, 4, 1),   # 769 tiles: correction form, 2 tiles
+    ("t4_ragged_asym_m16", 16400, 1024, 16, 0),  # 1025 tiles, 4 per workgroup
 ]
-
 
 @pytest.mark.parametrize("name,n,k,m,fmt", MULTI_TILE_CASES, ids=[c[0] for c in MULTI_TILE_CASES])
 def test_gemv_several_tiles_per_workgroup(name, n, k, m, fmt):
     L = Layer(n, k, m, fmt, config=6, rows=np.arange(n))
-    L.check(awq.awq_gemv(to_dev(L.x), L.inv, L.packed, n, k, 128, fmt))
+    y = awq.awq_gemv(to_dev(L.x), L.inv, L.packed, n, k, 128, fmt)
+    L.check(y)
+    # up to 768 row tiles awq_gemm takes the same kernel on these shapes: the same bits
+    if n // 16 <= 768:
+        assert awq.awq_workspace_bytes(m, n, k) == 0
+        y2 = awq.awq_gemm(to_dev(L.x), L.inv, L.packed, n, k, 128, fmt)
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
 
 # ----------------------------------------------------------- awq_gemm narrow tilings
