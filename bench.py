@@ -606,10 +606,40 @@ def ceilings(dev, sizes, graph_us, rotation):
         del buf
         torch.cuda.empty_cache()
     out["empty_launch_us"] = round(graph_us([lambda: probe.awq_probe_empty(stream())] * 100, 20), 3)
+    # matrix-core / ALU co-issue: 8 matrix instructions per iteration, each followed by
+    # 0 .. 4 packed binary16 multiplies, one or two wavefronts per SIMD on every CU
+    probe.awq_probe_mfma_alu.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_void_p]
+    iters = 4000
+    co = torch.empty(512 * 256, dtype=torch.float32, device=dev)
+    coissue = {}
+    for blocks, label in ((256, "one_wave_per_simd"), (512, "two_waves_per_simd")):
+        row = {}
+        for alu in range(5):
+            for _ in range(3):
+                probe.awq_probe_mfma_alu(co.data_ptr(), alu, blocks, iters, stream())
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                probe.awq_probe_mfma_alu(co.data_ptr(), alu, blocks, iters, stream())
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / 5
+            mfma = blocks * 4 * iters * 8
+            row[f"alu_{alu}"] = {"us": round(us, 1),
+                                 "TFLOP/s": round(mfma * 16384 / us / 1e6, 1)}
+        base = row["alu_0"]["us"]
+        for alu in range(5):
+            row[f"alu_{alu}"]["slowdown"] = round(row[f"alu_{alu}"]["us"] / base, 3)
+        coissue[label] = row
+    out["mfma_alu_coissue"] = coissue
+    del co
     out["what"] = ("read-only kernel over the packed weight bytes of each decode shape, "
                    "16-byte non-temporal loads, 1 KiB per wavefront load, all loads of a "
                    "wavefront in flight; empty kernel back to back; graph-timed like the decode "
-                   "kernel")
+                   "kernel; mfma_alu_coissue: 8 independent 16x16x32 f16 matrix instructions per "
+                   "iteration, each followed by alu_N packed f16 multiplies, on 256 or 512 "
+                   "workgroups of 256 threads")
     return out
 
 

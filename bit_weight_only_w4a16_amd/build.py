@@ -50,6 +50,7 @@ FILE_FLAGS = {
     "gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=16"],
     "gemm_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=16"],
     "chain.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "ceilings.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

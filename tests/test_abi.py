@@ -44,7 +44,8 @@ def test_probe_library_exports_its_header():
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "awq_probe.h")).read(),
                   flags=re.S)
     names = sorted(set(re.findall(r"\b(awq_[a-z0-9_]+)\s*\(", text)))
-    assert names == ["awq_probe_empty", "awq_probe_shapes", "awq_probe_stream_read"]
+    assert names == ["awq_probe_empty", "awq_probe_mfma_alu", "awq_probe_shapes",
+                     "awq_probe_stream_read"]
     probe = ctypes.CDLL(B.PROBE_LIB)
     for n in names:
         assert hasattr(probe, n), n
@@ -54,6 +55,12 @@ def test_probe_library_exports_its_header():
     assert probe.awq_probe_stream_read(None, 1024, 0, None, None) == 1   # checked before launch
     assert probe.awq_probe_stream_read(16, 1 << 31, 0, 16, None) == 1
     assert probe.awq_probe_stream_read(8, 1024, 0, 16, None) == 3
+    probe.awq_probe_mfma_alu.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_void_p]
+    assert probe.awq_probe_mfma_alu(None, 0, 256, 10, None) == 1
+    assert probe.awq_probe_mfma_alu(16, 5, 256, 10, None) == 1
+    assert probe.awq_probe_mfma_alu(16, 0, 0, 10, None) == 1
+    assert probe.awq_probe_mfma_alu(16, 0, 4097, 10, None) == 1
 
 
 def test_gemm_noalloc_checks_before_any_launch(lib):
