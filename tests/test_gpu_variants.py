@@ -138,6 +138,26 @@ def test_gemv_several_tiles_per_workgroup(name, n, k, m, fmt):
         assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
 
+# ------------------------------------------------ wide tiles: banded block order
+
+# M = 1100 gives 9 row blocks of 128: one full band of 8 row blocks and a band of one.
+# (name, N, K, M, fmt): 128 x 256 tiles (513 blocks), 128 x 192 tiles (522 blocks), and
+# 128 x 192 tiles with K halves inside the workgroup and K split over two workgroups
+# (99 blocks).
+BAND_CASES = [
+    ("band_wn4_asym", 14592, 512, 1100, 0),
+    ("band_wn3_sym", 11136, 512, 1100, 1),
+    ("band_ks2_sym", 2048, 1024, 1100, 1),
+]
+
+
+@pytest.mark.parametrize("name,n,k,m,fmt", BAND_CASES, ids=[c[0] for c in BAND_CASES])
+def test_wide_gemm_partial_band(name, n, k, m, fmt):
+    L = Layer(n, k, m, fmt, config=5)
+    ws = awq.workspace(m, n, k, DEV)
+    L.check(awq.awq_gemm(to_dev(L.x), L.inv, L.packed, n, k, 128, fmt, ws=ws))
+
+
 # ----------------------------------------------------------- awq_gemm narrow tilings
 
 # M = 48 on a layer of more than 2^26 weights: 64 x 128 workgroup tiles, K split;
