@@ -158,6 +158,26 @@ __global__ void __launch_bounds__(256 * KS) gemm_wide_kernel(WideArgs a) {
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[i][j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // The unpack constants live in registers whose values the compiler does not see (mask
+  // in an SGPR, magic in a VGPR), so (w & mask) | magic stays one ordinary v_and_or_b32:
+  // an instruction the scheduler can place between matrix instructions and whose
+  // read-after-write distance to them it tracks (gfx9 VOP3 takes no literal constants).
+  uint32_t mask0, mask1, magic0, magic1;
+  asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(mask0));
+  asm volatile("s_mov_b32 %0, 0x00F000F0" : "=s"(mask1));
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic0));
+  asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(magic1));
+  // exact dequantization of one word (eight weights of one column): (off + q) - (off + z)
+  // is an exact small integer, times s rounded once to binary16
+  auto deq = [&](uint32_t w, uint32_t nz1024, uint32_t nz64, half2_t s2) -> half8_t {
+    const uint32_t w8 = w >> 8;
+    const half2_t d0 = (as_h2((w & mask0) | magic0) + as_h2(nz1024)) * s2;
+    const half2_t d1 = (as_h2((w & mask1) | magic1) + as_h2(nz64)) * s2;
+    const half2_t d2 = (as_h2((w8 & mask0) | magic0) + as_h2(nz1024)) * s2;
+    const half2_t d3 = (as_h2((w8 & mask1) | magic1) + as_h2(nz64)) * s2;
+    return half8_t{d0.x, d0.y, d1.x, d1.y, d2.x, d2.y, d3.x, d3.y};
+  };
+
   auto compute = [&](const BRegs& b, int buf) {
     const unsigned char* src = smem + buf * kTileBytes;
     half2_t s2[WN];
@@ -169,30 +189,56 @@ __global__ void __launch_bounds__(256 * KS) gemm_wide_kernel(WideArgs a) {
       nz1024[j] = neg_off1024(z);
       nz64[j] = neg_off64(z);
     }
-    // k-step i: the eight A fragments (row 16 ms + r, chunk 4 p + i, swizzled) are read
-    // first; then each column fragment is dequantized right before its eight matrix
-    // instructions, so the ALU work of the next column overlaps the matrix core's work on
-    // this one. With three columns a scheduling fence after each column keeps that order
-    // (measured: 2-3 % faster there, no gain with two or four).
+    auto word = [&](int i, int j) -> uint32_t {
+      return i == 0 ? b.c[j].x : i == 1 ? b.c[j].y : i == 2 ? b.c[j].z : b.c[j].w;
+    };
+    // A fragment of row tile ms at k-step i: row 16 ms + r, chunk 4 p + i (swizzled)
+    auto afrag = [&](int i, int ms) -> half8_t {
+      const int chunk = (4 * p + i) ^ r;
+      return *reinterpret_cast<const half8_t*>(src + (16 * ms + r) * kRowBytes + 16 * chunk);
+    };
+    // Software pipeline over the (k-step, column) blocks of the group: while column j of
+    // k-step i is multiplied (eight matrix instructions, one per row tile), the next
+    // column's weights (or column 0 of k-step i + 1) are dequantized, and during the last
+    // column of a k-step the next k-step's X' fragments are read, each right after its
+    // last use. Scheduling groups place one matrix instruction, then up to two ALU
+    // instructions and one LDS read, so that a wavefront's ALU work issues while its own
+    // matrix instructions run (about two ALU instructions fit under one): matrix-core
+    // busy 0.59 -> 0.62 and co-issued cycles 0.22 -> 0.35 of it on 4096 -> 28672 at
+    // M = 2048, with the same sums in the same order.
+    half8_t af[WM];
+#pragma unroll
+    for (int ms = 0; ms < WM; ++ms) af[ms] = afrag(0, ms);
+    half8_t bcur = deq(word(0, 0), nz1024[0], nz64[0], s2[0]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int chunk = (4 * p + i) ^ r;
-      half8_t af[WM];
-#pragma unroll
-      for (int ms = 0; ms < WM; ++ms) {
-        af[ms] = *reinterpret_cast<const half8_t*>(src + (16 * ms + r) * kRowBytes + 16 * chunk);
-      }
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
-        const uint32_t w = i == 0 ? b.c[j].x : i == 1 ? b.c[j].y : i == 2 ? b.c[j].z : b.c[j].w;
-        half2_t d[4];
-        dequant_word(w, nz1024[j], nz64[j], s2[j], d);
-        const half8_t bf = {d[0].x, d[0].y, d[1].x, d[1].y, d[2].x, d[2].y, d[3].x, d[3].y};
+        const bool last = j == WN - 1;
+        const int ni = last ? i + 1 : i, nj = last ? 0 : j + 1;
+        half8_t bnext = bcur;
+        if (ni < 4) bnext = deq(word(ni, nj), nz1024[nj], nz64[nj], s2[nj]);
 #pragma unroll
         for (int ms = 0; ms < WM; ++ms) {
-          acc[ms][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[ms], bf, acc[ms][j], 0, 0, 0);
+          acc[ms][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[ms], bcur, acc[ms][j], 0, 0, 0);
+          if (last && i < 3) af[ms] = afrag(i + 1, ms);
         }
-        if constexpr (WN == 3) __builtin_amdgcn_sched_barrier(0);
+        // 13 ALU instructions of the next dequantization: 2, 2, 2, 2, 2, 1, 1, 1
+#pragma unroll
+        for (int ms = 0; ms < WM; ++ms) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix instruction
+          if (ni < 4) {
+            if (ms < 5) {
+              __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // ALU
+            } else {
+              __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+            }
+          }
+          if (last && i < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        bcur = bnext;
       }
     }
   };
